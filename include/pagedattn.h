@@ -1,0 +1,166 @@
+/*
+ * pagedattn.h - C ABI of the MI355X (gfx950) paged-decode library
+ * (libpagedattn.so).
+ *
+ * Two operations, after the pages this library follows:
+ *   [KVP]   "PagedAttention：KV Cache 的分页革命" (openeuler.csdn.net)
+ *   [INFRA] "【infra之路】10-PagedAttention 与 KV Cache 管理" (jsqmd.com)
+ *   [OPS]   the l189.com article on the ops-transformer PagedAttention
+ *           operator for the Ascend NPU
+ *
+ * pa_reshape_and_cache writes each new token's K and V rows into the physical
+ * slot named for it ([INFRA] §1.2: the step appends the new token's K and V to
+ * the cache; §3.3: the token goes into the next slot of the request's last
+ * block, a new block being appended to the table when that one is full).
+ *
+ * pa_decode is decode-phase attention over a paged cache ([INFRA] §1.1: the new
+ * token's query of each head is scored against every cached key, scaled,
+ * normalised by a softmax, and the weights average the cached values; §3.3 and
+ * §3.4: the cached rows are found through the request's block table, which is
+ * passed to the kernel, Q1 of §8).
+ *
+ * Layouts (all row-major, contiguous, element type `dtype`):
+ *   q, out        [num_seqs, num_q_heads, head_dim]
+ *   key, value    [num_tokens, num_kv_heads, head_dim]
+ *   k_cache,
+ *   v_cache       [num_blocks, num_kv_heads, block_size, head_dim]
+ *                 (one (block, kv head) tile is block_size*head_dim contiguous
+ *                 elements; K and V are separate pools, as [OPS] keeps the K
+ *                 and V halves of a page apart)
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq]; entry j of row s is
+ *                 the physical block holding tokens j*block_size ..
+ *                 j*block_size + block_size - 1 of sequence s
+ *   context_lens  int32 [num_seqs]; tokens attended by each sequence
+ *   slot_mapping  int32 [num_tokens]; slot = block * block_size + offset,
+ *                 negative = write nothing for that token
+ *
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads) (grouped-query
+ * attention with contiguous groups; [INFRA] §2.1 names 8 KV heads for 32
+ * query heads).
+ *
+ * Ownership and threading: every pointer argument is a device pointer owned by
+ * the caller (except where stated). The library allocates, frees and
+ * synchronises nothing; it keeps no state between calls. Work is enqueued on
+ * `stream` (a hipStream_t; NULL is the null stream) and runs asynchronously.
+ * Calls on different streams touching the same buffers race as any two
+ * kernels would.
+ *
+ * Errors: arguments are checked on the host before anything is enqueued; on a
+ * non-zero status nothing was enqueued (except PA_ERR_HIP, which reports a
+ * launch failure). Values that live in device memory (table entries in
+ * [0, num_blocks), 1 <= context_lens[s] <= max_context_len, distinct slots)
+ * are preconditions; they are checked only when the environment variable
+ * PA_DEBUG is set to a non-zero value, in which case the call copies them to
+ * the host (synchronising the stream) and returns PA_ERR_BAD_INDEX on a
+ * violation. A context length of 0 yields an all-zero output row.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+  PA_OK = 0,
+  PA_ERR_NULL_POINTER = 1,       /* a required pointer is NULL */
+  PA_ERR_BAD_SHAPE = 2,          /* a size is out of range or inconsistent */
+  PA_ERR_UNSUPPORTED = 3,        /* head_dim, block_size, dtype or group not built */
+  PA_ERR_WORKSPACE_TOO_SMALL = 4,
+  PA_ERR_HIP = 5,                /* the HIP runtime reported an error */
+  PA_ERR_BAD_INDEX = 6           /* PA_DEBUG: a device-side precondition failed */
+};
+
+/* Element types of q, out, key, value and the pools (all the same). */
+enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 };
+
+/*
+ * pa_reshape_and_cache - copy new tokens' K/V rows into the pools.
+ *
+ * For every token t with slot = slot_mapping[t] >= 0, copies key[t, h, :] to
+ * k_cache[slot / block_size, h, slot % block_size, :] and value[t, h, :] to
+ * the same place of v_cache, for every KV head h. The copy is bit-exact (no
+ * conversion). Slots must be distinct and < num_blocks * block_size (checked
+ * under PA_DEBUG only).
+ *
+ * Supported: head_dim in {64, 128, 256}, block_size in {8, 16, 32, 64},
+ * dtype in {PA_F32, PA_F16, PA_BF16}. num_tokens may be 0 (no launch).
+ */
+int32_t pa_reshape_and_cache(const void *key, const void *value, void *k_cache,
+                             void *v_cache, const int32_t *slot_mapping,
+                             int32_t num_tokens, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t dtype, void *stream);
+
+/*
+ * pa_decode_workspace_size - device scratch bytes pa_decode needs.
+ *
+ * The context of each sequence is cut into partitions of `partition_size`
+ * tokens (0 = the library's default for these shapes); each partition is
+ * processed by its own workgroup and, when a sequence has more than one,
+ * the partial results are combined by a log-sum-exp reduction (split-K in the
+ * manner of flash decoding, [INFRA] Q2 of §8). Returns 0 when max_context_len
+ * fits in one partition, and (size_t)-1 for arguments pa_decode would reject.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t partition_size,
+                                int32_t dtype);
+
+/*
+ * pa_decode_partition_size - the partition size pa_decode will use.
+ *
+ * `requested` = 0 picks the library default for the shapes; otherwise it must
+ * be a positive multiple of 16 and is returned unchanged. Returns -1 for
+ * arguments pa_decode would reject.
+ */
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t requested,
+                                 int32_t dtype);
+
+/*
+ * pa_decode - one decode step of paged attention.
+ *
+ * out[s, h, :] = sum_i p_i * V_s[i, :] with p = softmax(scale * K_s q[s, h]),
+ * where K_s and V_s are the first context_lens[s] rows of KV head
+ * h / (num_q_heads / num_kv_heads), gathered through block_tables[s].
+ * Accumulation is float32; out is rounded once to `dtype` (nearest even).
+ * Slots past a sequence's context and table entries past its last block are
+ * never read.
+ *
+ * scale            the softmax scale (1/sqrt(head_dim) for standard attention)
+ * max_context_len  max over s of context_lens[s] (host value: sizes the grid)
+ * partition_size   0 = default, else a multiple of 16 (see above)
+ * workspace        device scratch of at least pa_decode_workspace_size(...)
+ *                  bytes (may be NULL when that size is 0); its contents on
+ *                  entry do not matter
+ *
+ * Supported: head_dim in {64, 128, 256}; block_size in {8, 16, 32, 64};
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8}; dtype in {PA_F32, PA_F16,
+ * PA_BF16}; max_context_len <= max_blocks_per_seq * block_size.
+ */
+int32_t pa_decode(void *out, const void *q, const void *k_cache,
+                  const void *v_cache, const int32_t *block_tables,
+                  const int32_t *context_lens, float scale, int32_t num_seqs,
+                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t block_size, int32_t num_blocks,
+                  int32_t max_blocks_per_seq, int32_t max_context_len,
+                  int32_t partition_size, int32_t dtype, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/* A static, human-readable name of a status code. */
+const char *pa_status_str(int32_t status);
+
+/* Library ABI version (bumped on any signature change). */
+int32_t pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,54 @@
+"""ctypes loader for libpagedattn.so (the C ABI in include/pagedattn.h).
+
+Loading needs only the HIP runtime library, not a GPU. The library is never
+rebuilt here: a missing library raises, it is not replaced by anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+
+_i32 = ctypes.c_int32
+_ptr = ctypes.c_void_p
+_f32 = ctypes.c_float
+_size = ctypes.c_size_t
+
+# name -> (restype, argtypes), mirroring include/pagedattn.h
+SIGNATURES = {
+    "pa_reshape_and_cache": (_i32, [_ptr, _ptr, _ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _i32,
+                                    _i32, _ptr]),
+    "pa_decode_workspace_size": (_size, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode": (_i32, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _f32, _i32, _i32, _i32, _i32, _i32,
+                         _i32, _i32, _i32, _i32, _i32, _ptr, _size, _ptr]),
+    "pa_status_str": (ctypes.c_char_p, [_i32]),
+    "pa_abi_version": (_i32, []),
+}
+
+_LIB = None
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise LibraryNotBuilt(
+                f"{LIB_PATH} is missing; build it with `python -m paged_kv_cache_362_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def status_str(code: int) -> str:
+    return lib().pa_status_str(code).decode()

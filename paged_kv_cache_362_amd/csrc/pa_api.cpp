@@ -1,0 +1,239 @@
+// pa_api.cpp - the C ABI of libpagedattn.so: argument checks, the partition
+// policy, workspace sizing and the optional (PA_DEBUG) device-side checks.
+// Declarations and the contract of every entry point are in
+// include/pagedattn.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <unordered_set>
+#include <vector>
+
+#include "pa_internal.h"
+#include "pagedattn.h"
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+
+bool debug_checks() {
+  const char *e = std::getenv("PA_DEBUG");
+  return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
+}
+
+int elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PA_F32: return 4;
+    case PA_F16: return 2;
+    case PA_BF16: return 2;
+  }
+  return 0;
+}
+
+int exact_log2(int32_t x) {
+  if (x <= 0 || (x & (x - 1)) != 0) return -1;
+  int s = 0;
+  while ((1 << s) != x) ++s;
+  return s;
+}
+
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128 || d == 256; }
+bool block_size_ok(int32_t b) { return b == 8 || b == 16 || b == 32 || b == 64; }
+bool group_ok(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by pa_decode and its sizing helpers.
+int32_t check_decode_shapes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t max_context_len, int32_t dtype) {
+  if (num_seqs < 0 || num_seqs > 65535 || num_kv_heads <= 0 || num_kv_heads > 65535 ||
+      num_q_heads <= 0 || max_context_len < 0)
+    return PA_ERR_BAD_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return PA_ERR_BAD_SHAPE;
+  if (elem_bytes(dtype) == 0 || !head_dim_ok(head_dim) || !group_ok(num_q_heads / num_kv_heads))
+    return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+int32_t resolve_partition(int32_t requested) {
+  if (requested == 0) return pa::kDefaultPartition;
+  if (requested < 16 || requested > pa::kMaxPartition || requested % 16 != 0) return -1;
+  return requested;
+}
+
+int32_t num_partitions(int32_t max_context_len, int32_t partition) {
+  const int32_t np = (max_context_len + partition - 1) / partition;
+  return np < 1 ? 1 : np;
+}
+
+size_t workspace_bytes_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                           int32_t max_partitions) {
+  if (max_partitions <= 1) return 0;
+  const size_t rows = size_t(num_seqs) * size_t(num_q_heads) * size_t(max_partitions);
+  return rows * size_t(head_dim + 2) * sizeof(float);
+}
+
+int32_t sync_copy_to_host(void *dst, const void *src, size_t bytes, hipStream_t stream) {
+  if (bytes == 0) return PA_OK;
+  if (hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return PA_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return PA_ERR_HIP;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_abi_version(void) { return kAbiVersion; }
+
+const char *pa_status_str(int32_t status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL_POINTER: return "null pointer argument";
+    case PA_ERR_BAD_SHAPE: return "bad or inconsistent shape argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, dtype, group or alignment";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_BAD_INDEX: return "device-side index precondition violated (PA_DEBUG)";
+  }
+  return "unknown status";
+}
+
+int32_t pa_reshape_and_cache(const void *key, const void *value, void *k_cache, void *v_cache,
+                             const int32_t *slot_mapping, int32_t num_tokens,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t dtype, void *stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return PA_ERR_BAD_SHAPE;
+  if (elem_bytes(dtype) == 0 || !head_dim_ok(head_dim) || !block_size_ok(block_size))
+    return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL_POINTER;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t num_slots = int64_t(num_blocks) * block_size;
+
+  if (debug_checks()) {
+    std::vector<int32_t> slots(num_tokens);
+    int32_t st = sync_copy_to_host(slots.data(), slot_mapping, sizeof(int32_t) * num_tokens, s);
+    if (st != PA_OK) return st;
+    std::unordered_set<int32_t> seen;
+    for (int32_t v : slots) {
+      if (v < 0) continue;
+      if (v >= num_slots || !seen.insert(v).second) return PA_ERR_BAD_INDEX;
+    }
+  }
+
+  pa::CacheParams p{};
+  p.key = key;
+  p.value = value;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.slot_mapping = slot_mapping;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = num_kv_heads;
+  p.row_chunks = head_dim * elem_bytes(dtype) / 16;
+  p.block_shift = exact_log2(block_size);
+  p.num_slots = num_slots;
+  return pa::launch_reshape_and_cache(p, s) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len, int32_t requested,
+                                 int32_t dtype) {
+  if (check_decode_shapes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                          dtype) != PA_OK)
+    return -1;
+  return resolve_partition(requested);
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_context_len,
+                                int32_t partition_size, int32_t dtype) {
+  if (check_decode_shapes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                          dtype) != PA_OK)
+    return size_t(-1);
+  const int32_t part = resolve_partition(partition_size);
+  if (part < 0) return size_t(-1);
+  return workspace_bytes_for(num_seqs, num_q_heads, head_dim,
+                             num_partitions(max_context_len, part));
+}
+
+int32_t pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                  const int32_t *block_tables, const int32_t *context_lens, float scale,
+                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                  int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size,
+                  int32_t dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  int32_t st = check_decode_shapes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                   max_context_len, dtype);
+  if (st != PA_OK) return st;
+  if (!block_size_ok(block_size)) return PA_ERR_UNSUPPORTED;
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0) return PA_ERR_BAD_SHAPE;
+  if (int64_t(max_context_len) > int64_t(max_blocks_per_seq) * block_size) return PA_ERR_BAD_SHAPE;
+  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+    return PA_ERR_BAD_SHAPE;
+  const int32_t part = resolve_partition(partition_size);
+  if (part < 0) return PA_ERR_BAD_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_NULL_POINTER;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
+  const int32_t max_parts = num_partitions(max_context_len, part);
+  const size_t need = workspace_bytes_for(num_seqs, num_q_heads, head_dim, max_parts);
+  if (need > 0) {
+    if (!workspace) return PA_ERR_NULL_POINTER;
+    if (workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned16(workspace)) return PA_ERR_UNSUPPORTED;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  if (debug_checks()) {
+    std::vector<int32_t> lens(num_seqs);
+    std::vector<int32_t> tab(size_t(num_seqs) * max_blocks_per_seq);
+    st = sync_copy_to_host(lens.data(), context_lens, sizeof(int32_t) * lens.size(), s);
+    if (st != PA_OK) return st;
+    st = sync_copy_to_host(tab.data(), block_tables, sizeof(int32_t) * tab.size(), s);
+    if (st != PA_OK) return st;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      const int32_t n = lens[i];
+      if (n < 0 || n > max_context_len) return PA_ERR_BAD_INDEX;
+      const int32_t used = (n + block_size - 1) / block_size;
+      for (int32_t j = 0; j < used; ++j) {
+        const int32_t b = tab[size_t(i) * max_blocks_per_seq + j];
+        if (b < 0 || b >= num_blocks) return PA_ERR_BAD_INDEX;
+      }
+    }
+  }
+
+  pa::DecodeParams p{};
+  p.out = out;
+  if (need > 0) {
+    const size_t rows = size_t(num_seqs) * num_q_heads * max_parts;
+    float *ws = static_cast<float *>(workspace);
+    p.ws_acc = ws;
+    p.ws_m = ws + rows * head_dim;
+    p.ws_l = p.ws_m + rows;
+  }
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.scale_log2 = float(double(scale) * 1.4426950408889634074);
+  p.num_seqs = num_seqs;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_q_heads / num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_shift = exact_log2(block_size);
+  p.num_blocks = num_blocks;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_context_len = max_context_len;
+  p.partition_size = part;
+  p.max_partitions = max_parts;
+  p.dtype = dtype;
+  return pa::launch_decode(p, s) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+"""Python binding of libpagedattn.so on torch tensors (argument marshalling only).
+
+torch supplies device memory and the current HIP stream; every step of the
+computation runs in the library's HIP kernels. There is no fallback: when the
+library is missing or the tensors are not on a GPU, these functions raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import lib, status_str
+
+DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+PA_OK = 0
+STATUS = {0: "PA_OK", 1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_BAD_SHAPE", 3: "PA_ERR_UNSUPPORTED",
+          4: "PA_ERR_WORKSPACE_TOO_SMALL", 5: "PA_ERR_HIP", 6: "PA_ERR_BAD_INDEX"}
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)} ({status_str(code)})")
+        self.code = code
+
+
+def _check(fn: str, code: int) -> None:
+    if code != PA_OK:
+        raise PagedAttentionError(fn, code)
+
+
+def _dev_ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _on_gpu(*ts: torch.Tensor) -> None:
+    dev = ts[0].device
+    for t in ts:
+        _require(t.is_cuda, "tensors must live on a GPU")
+        _require(t.device == dev, "tensors must live on one GPU")
+        _require(t.is_contiguous(), "tensors must be contiguous")
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    if dtype not in DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {dtype}")
+    return DTYPE_CODE[dtype]
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
+    """Write key/value [T, Hkv, D] into the pools [N, Hkv, B, D] at slot_mapping [T]."""
+    _on_gpu(key, value, k_cache, v_cache, slot_mapping)
+    _require(key.dim() == 3 and value.shape == key.shape, "key/value must be [T, Hkv, D]")
+    _require(k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "pools must be [N, Hkv, B, D]")
+    _require(key.dtype == value.dtype == k_cache.dtype == v_cache.dtype, "one dtype for all")
+    _require(slot_mapping.dtype == torch.int32 and slot_mapping.shape == (key.shape[0],),
+             "slot_mapping must be int32 [T]")
+    n, hkv, bs, d = k_cache.shape
+    _require(key.shape[1:] == (hkv, d), "key heads/dim must match the pools")
+    code = lib().pa_reshape_and_cache(
+        _dev_ptr(key), _dev_ptr(value), _dev_ptr(k_cache), _dev_ptr(v_cache),
+        _dev_ptr(slot_mapping), key.shape[0], hkv, d, bs, n, dtype_code(key.dtype),
+        _stream(key))
+    _check("pa_reshape_and_cache", code)
+
+
+def partition_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                   max_context_len: int, dtype: torch.dtype, requested: int = 0) -> int:
+    p = lib().pa_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                       max_context_len, requested, dtype_code(dtype))
+    _require(p > 0, "invalid partition request")
+    return p
+
+
+def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                   max_context_len: int, dtype: torch.dtype, partition: int = 0) -> int:
+    size = lib().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                          max_context_len, partition, dtype_code(dtype))
+    _require(size != ctypes.c_size_t(-1).value, "invalid workspace request")
+    return size
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+           max_context_len: int, out: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None, partition: int = 0) -> torch.Tensor:
+    """Paged decode attention; returns out [S, Hq, D] in q's dtype.
+
+    ``max_context_len`` is the host-side maximum of ``context_lens``.
+    ``workspace`` (uint8, at least ``workspace_size(...)`` bytes) is allocated
+    here when not given.
+    """
+    _on_gpu(q, k_cache, v_cache, block_tables, context_lens)
+    _require(q.dim() == 3, "q must be [S, Hq, D]")
+    _require(k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "pools must be [N, Hkv, B, D]")
+    _require(q.dtype == k_cache.dtype == v_cache.dtype, "q and the pools share one dtype")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2,
+             "block_tables must be int32 [S, M]")
+    _require(context_lens.dtype == torch.int32 and context_lens.shape == (q.shape[0],),
+             "context_lens must be int32 [S]")
+    s, hq, d = q.shape
+    n, hkv, bs, d2 = k_cache.shape
+    _require(d == d2 and block_tables.shape[0] == s, "inconsistent shapes")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _on_gpu(out)
+        _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    need = workspace_size(s, hq, hkv, d, max_context_len, q.dtype, partition)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _on_gpu(workspace)
+    code = lib().pa_decode(
+        _dev_ptr(out), _dev_ptr(q), _dev_ptr(k_cache), _dev_ptr(v_cache),
+        _dev_ptr(block_tables), _dev_ptr(context_lens), float(scale), s, hq, hkv, d, bs, n,
+        block_tables.shape[1], int(max_context_len), int(partition), dtype_code(q.dtype),
+        _dev_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
+    _check("pa_decode", code)
+    return out

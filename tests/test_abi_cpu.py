@@ -1,0 +1,108 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching a GPU (CPU only: no compute call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_362_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+F32, F16, BF16 = 0, 1, 2
+OK, NULLP, SHAPE, UNSUP, WS = 0, 1, 2, 3, 4
+BAD_SIZE = ctypes.c_size_t(-1).value
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libpagedattn.so is not built (python -m paged_kv_cache_362_amd.build)")
+    return _lib.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("pa_reshape_and_cache", "pa_decode", "pa_decode_workspace_size",
+              "pa_decode_partition_size", "pa_status_str", "pa_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} missing from libpagedattn.so"
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_status_strings_and_version(lib):
+    assert lib.pa_abi_version() == 1
+    for code in range(7):
+        assert lib.pa_status_str(code)
+    assert lib.pa_status_str(99) == b"unknown status"
+
+
+def test_partition_policy(lib):
+    assert lib.pa_decode_partition_size(32, 32, 32, 128, 2048, 0, F16) == 256
+    assert lib.pa_decode_partition_size(32, 32, 32, 128, 2048, 64, F16) == 64
+    assert lib.pa_decode_partition_size(32, 32, 32, 128, 2048, 24, F16) == -1
+    assert lib.pa_decode_partition_size(32, 32, 32, 128, 2048, 4096, F16) == -1
+    assert lib.pa_decode_partition_size(32, 32, 32, 96, 2048, 0, F16) == -1
+
+
+def test_workspace_size(lib):
+    # one partition: nothing needed
+    assert lib.pa_decode_workspace_size(4, 8, 8, 128, 256, 256, F16) == 0
+    # S * Hq * partitions * (D + 2) * 4
+    assert lib.pa_decode_workspace_size(32, 32, 32, 128, 2048, 256, F16) == 32 * 32 * 8 * 130 * 4
+    assert lib.pa_decode_workspace_size(1, 32, 32, 64, 8192, 0, F16) == 32 * 32 * 66 * 4
+    assert lib.pa_decode_workspace_size(1, 6, 4, 64, 100, 0, F16) == BAD_SIZE  # 6 % 4
+    assert lib.pa_decode_workspace_size(1, 12, 4, 64, 100, 0, F16) == BAD_SIZE  # group 3
+    assert lib.pa_decode_workspace_size(1, 4, 4, 64, 100, 0, 7) == BAD_SIZE  # dtype
+
+
+def _decode(lib, **kw):
+    a = dict(out=16, q=16, k=16, v=16, bt=16, cl=16, scale=0.125, S=1, Hq=4, Hkv=4, D=64,
+             B=16, N=4, M=4, maxlen=50, part=0, dtype=F32, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.pa_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["scale"], a["S"],
+                         a["Hq"], a["Hkv"], a["D"], a["B"], a["N"], a["M"], a["maxlen"],
+                         a["part"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_decode_rejects_bad_arguments_before_launch(lib):
+    # The fake (aligned, non-null) pointers are never dereferenced: every call
+    # below fails host validation first.
+    assert _decode(lib, q=None) == NULLP
+    assert _decode(lib, Hq=6) == SHAPE
+    assert _decode(lib, Hq=12) == UNSUP
+    assert _decode(lib, D=96) == UNSUP
+    assert _decode(lib, B=12) == UNSUP
+    assert _decode(lib, dtype=5) == UNSUP
+    assert _decode(lib, maxlen=65) == SHAPE  # > M * B
+    assert _decode(lib, N=0) == SHAPE
+    assert _decode(lib, part=20) == SHAPE
+    assert _decode(lib, scale=float("nan")) == SHAPE
+    assert _decode(lib, q=24) == UNSUP  # misaligned
+    assert _decode(lib, maxlen=50, part=16) == NULLP  # needs a workspace
+    assert _decode(lib, maxlen=50, part=16, ws=16, wsb=10) == WS
+    assert _decode(lib, S=0, q=None, out=None) == OK  # empty batch: no work, no launch
+
+
+def test_cache_write_rejects_bad_arguments_before_launch(lib):
+    # as above: every call fails host validation (or has no work) before any launch
+    f = lib.pa_reshape_and_cache
+    assert f(16, 16, 16, 16, None, 1, 4, 64, 16, 8, F16, None) == NULLP
+    assert f(16, 16, 16, 16, 16, -1, 4, 64, 16, 8, F16, None) == SHAPE
+    assert f(16, 16, 16, 16, 16, 1, 4, 80, 16, 8, F16, None) == UNSUP
+    assert f(16, 16, 16, 16, 16, 1, 4, 64, 24, 8, F16, None) == UNSUP
+    assert f(16, 16, 24, 16, 16, 1, 4, 64, 16, 8, F16, None) == UNSUP
+    assert f(None, None, None, None, None, 0, 4, 64, 16, 8, F16, None) == OK

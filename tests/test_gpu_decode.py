@@ -1,0 +1,283 @@
+"""GPU parity of pa_decode (and the cache write feeding it) against the oracle.
+
+Runs the HIP library through its C ABI (via the ctypes binding) on an MI355X.
+Tolerances are those of tests/parity.py.
+
+[INFRA] "【infra之路】10-PagedAttention 与 KV Cache 管理" (jsqmd.com)
+[KVP]   "PagedAttention：KV Cache 的分页革命" (openeuler.csdn.net)
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.paged_attention as O
+from paged_kv_cache_362_amd import layouts, ops
+from parity import assert_decode_close, gpu_step, oracle_step
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    yield
+    torch.cuda.synchronize()
+
+
+def _report(name, rep):
+    print(f"[parity] {name}: {rep}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads, scaled down (every output compared) and at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("partition", [0, 64])
+def test_scaled_config_parity(cfg, partition):
+    b = layouts.scaled_config(cfg, poison=True, max_seqs=4, max_len=700)
+    _, _, o64 = oracle_step(b)
+    _, out = gpu_step(b, partition=partition)
+    rep = assert_decode_close(layouts.from_device(out, b.dtype), o64, b.dtype, b.name)
+    _report(f"{b.name} P={partition}", rep)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_full_config_parity(cfg):
+    """Full-size workload, the launch the benchmark times (default partition).
+
+    Config 1 and 4 are compared in full; for 2, 3 and 5 eight sequences spread
+    over the batch (including the longest and shortest) are recomputed by the
+    oracle one by one.
+    """
+    b = layouts.make_config(cfg, poison=True)
+    if b.num_seqs <= 8:
+        seqs = np.arange(b.num_seqs)
+    else:
+        order = np.argsort(b.context_lens)
+        seqs = np.unique(np.concatenate([order[:2], order[-2:],
+                                         np.linspace(0, b.num_seqs - 1, 4).astype(int)]))
+    _, _, o64 = oracle_step(b, seqs)
+    t, out = gpu_step(b)
+    got = layouts.from_device(out, b.dtype)[seqs]
+    rep = assert_decode_close(got, o64, b.dtype, b.name)
+    _report(b.name, rep)
+    # the rest of the batch: finite, and unchanged under a rerun (deterministic)
+    assert not np.isnan(O.to_f64(layouts.from_device(out, b.dtype), b.dtype)).any()
+    out2 = ops.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                      t["context_lens"], b.scale, b.max_context_len)
+    assert torch.equal(out.view(torch.int16) if b.dtype != "f32" else out,
+                       out2.view(torch.int16) if b.dtype != "f32" else out2)
+
+
+# ---------------------------------------------------------------------------
+# the pages' worked examples
+# ---------------------------------------------------------------------------
+
+def _fixed_table_batch(table, n, dtype="f32", hq=4, hkv=4, d=64, bs=16, seed=5):
+    """One sequence whose table is given; pool 16 blocks, others poisoned."""
+    rng = np.random.default_rng(seed)
+    num_blocks = 16
+    q = layouts.draw(rng, (1, hq, d), dtype)
+    kc = layouts.draw(rng, (num_blocks, hkv, bs, d), dtype)
+    vc = layouts.draw(rng, (num_blocks, hkv, bs, d), dtype)
+    live = np.zeros((num_blocks, bs), bool)
+    for pos in range(n):
+        live[table[pos // bs], pos % bs] = True
+    nv = layouts.nan_value(dtype)
+    blk, off = np.nonzero(~live)
+    kc[blk, :, off, :] = nv
+    vc[blk, :, off, :] = nv
+    width = len(table) + 2
+    bt = np.full((1, width), [b for b in range(num_blocks) if b not in table][0], np.int32)
+    bt[0, :len(table)] = table
+    return layouts.PagedBatch(
+        dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs, q=q,
+        k_cache=kc, v_cache=vc, block_tables=bt, context_lens=np.array([n], np.int32),
+        new_key=np.zeros((0, hkv, d), kc.dtype), new_value=np.zeros((0, hkv, d), kc.dtype),
+        slot_mapping=np.zeros((0,), np.int32), scale=float(np.float32(1 / math.sqrt(d))),
+        seed=seed, poisoned=True, unique_blocks=len(table), name=f"table {table} n={n}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_worked_example_block_table(dtype):
+    g = json.load(open(os.path.join(GOLDEN, "worked_example_block_table.json")))
+    b = _fixed_table_batch(g["table"], g["context_len"], dtype)
+    o64 = O.ref_decode(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, b.scale, dtype)
+    _, out = gpu_step(b, write=False)
+    _report(b.name, assert_decode_close(layouts.from_device(out, dtype), o64, dtype, b.name))
+
+
+def test_page_table_example():
+    g = json.load(open(os.path.join(GOLDEN, "page_table_example.json")))
+    b = _fixed_table_batch(g["table"], g["context_len"], "f16")
+    o64 = O.ref_decode(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, b.scale, "f16")
+    _, out = gpu_step(b, write=False)
+    assert_decode_close(layouts.from_device(out, "f16"), o64, "f16", b.name)
+
+
+def test_51st_token_written_then_attended():
+    """Position 50 goes to block 12 offset 2 (slot 194); decode at n = 51."""
+    g = json.load(open(os.path.join(GOLDEN, "worked_example_block_table.json")))
+    b = _fixed_table_batch(g["table"], 51, "f32")
+    rng = np.random.default_rng(9)
+    b.new_key = layouts.draw(rng, (1, 4, 64), "f32")
+    b.new_value = layouts.draw(rng, (1, 4, 64), "f32")
+    b.slot_mapping = np.array([O.slot_of(g["table"], 50, 16)], np.int32)
+    assert b.slot_mapping[0] == g["position_50"]["slot"]
+    b.k_cache[12, :, 2, :] = np.nan  # the write must land before the read
+    b.v_cache[12, :, 2, :] = np.nan
+    _, _, o64 = oracle_step(b)
+    t, out = gpu_step(b)
+    assert_decode_close(layouts.from_device(out, "f32"), o64, "f32", "51st token")
+
+
+# ---------------------------------------------------------------------------
+# shapes, lengths and partitions
+# ---------------------------------------------------------------------------
+
+SHAPES = [
+    # dtype, Hq, Hkv, D, B
+    ("f16", 8, 8, 128, 16), ("bf16", 8, 2, 128, 16), ("f32", 4, 4, 64, 16),
+    ("f16", 8, 1, 64, 8), ("bf16", 16, 2, 64, 32), ("f16", 4, 2, 256, 64),
+    ("f32", 8, 4, 128, 32), ("bf16", 2, 2, 256, 8), ("f32", 8, 1, 256, 16),
+]
+EDGE_LENS = [1, 2, 15, 16, 17, 31, 33, 63, 64, 65, 255, 256, 257, 511, 513, 1000]
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,d,bs", SHAPES)
+def test_shapes_and_ragged_lengths(dtype, hq, hkv, d, bs):
+    lens = np.array(EDGE_LENS, np.int32)
+    b = layouts.make_paged_batch(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, dtype=dtype,
+                                 block_size=bs, context_lens=lens, seed=21, poison=True,
+                                 extra_table_cols=2, name=f"{dtype} {hq}/{hkv} D{d} B{bs}")
+    _, _, o64 = oracle_step(b)
+    for partition in (0, 16, 48, 512):
+        _, out = gpu_step(b, partition=partition)
+        rep = assert_decode_close(layouts.from_device(out, dtype), o64, dtype,
+                                  f"{b.name} P={partition}")
+    _report(b.name, rep)
+
+
+def test_long_context_max_partition():
+    """A 65536-token sequence (longest tested), default and largest partition."""
+    lens = np.array([65536, 3], np.int32)
+    b = layouts.make_paged_batch(num_q_heads=8, num_kv_heads=8, head_dim=128, dtype="f16",
+                                 block_size=16, context_lens=lens, seed=22, poison=False)
+    _, _, o64 = oracle_step(b)
+    for partition in (0, 2048):
+        _, out = gpu_step(b, partition=partition)
+        assert_decode_close(layouts.from_device(out, "f16"), o64, "f16", f"64K P={partition}")
+
+
+# ---------------------------------------------------------------------------
+# invariants and closed forms on the GPU
+# ---------------------------------------------------------------------------
+
+def test_block_permutation_is_bit_identical():
+    b = layouts.scaled_config(2, max_seqs=4, max_len=700)
+    _, out1 = gpu_step(b)
+    perm = np.random.default_rng(3).permutation(b.num_blocks)
+    kc = np.empty_like(b.k_cache)
+    vc = np.empty_like(b.v_cache)
+    kc[perm] = b.k_cache
+    vc[perm] = b.v_cache
+    b2 = layouts.PagedBatch(**{**b.__dict__, "k_cache": kc, "v_cache": vc,
+                               "block_tables": perm[b.block_tables].astype(np.int32),
+                               "slot_mapping": (perm[b.slot_mapping // b.block_size] * b.block_size
+                                                + b.slot_mapping % b.block_size).astype(np.int32)})
+    _, out2 = gpu_step(b2)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+def test_poisoned_pads_do_not_change_output():
+    clean = layouts.scaled_config(3, max_seqs=4, max_len=700, poison=False)
+    dirty = layouts.scaled_config(3, max_seqs=4, max_len=700, poison=True)
+    _, o1 = gpu_step(clean)
+    _, o2 = gpu_step(dirty)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_constant_values_give_exactly_one():
+    b = layouts.scaled_config(2, max_seqs=4, max_len=700)
+    b.k_cache = b.k_cache.copy()
+    b.v_cache = np.ones_like(b.v_cache)
+    b.new_value = np.ones_like(b.new_value)
+    for partition in (0, 64):
+        _, out = gpu_step(b, partition=partition)
+        assert torch.all(out == 1.0)
+
+
+def test_single_token_returns_its_value_exactly():
+    b = layouts.make_paged_batch(num_q_heads=8, num_kv_heads=4, head_dim=128, dtype="bf16",
+                                 block_size=16, context_lens=np.array([1, 1, 1]), seed=4)
+    _, out = gpu_step(b, write=False)
+    v = layouts.to_device(b)["v_cache"]
+    for s in range(3):
+        blk = int(b.block_tables[s, 0])
+        for h in range(8):
+            assert torch.equal(out[s, h], v[blk, h // 2, 0])
+
+
+def test_gqa_matches_repeated_mha():
+    """GQA with G=4 and MHA on the repeated KV heads agree with the same oracle values."""
+    b = layouts.scaled_config(3, max_seqs=3, max_len=500)
+    _, _, o64 = oracle_step(b)
+    _, o_gqa = gpu_step(b)
+    g = b.num_q_heads // b.num_kv_heads
+    mha = layouts.PagedBatch(**{**b.__dict__, "num_kv_heads": b.num_q_heads,
+                                "k_cache": np.repeat(b.k_cache, g, axis=1),
+                                "v_cache": np.repeat(b.v_cache, g, axis=1),
+                                "new_key": np.repeat(b.new_key, g, axis=1),
+                                "new_value": np.repeat(b.new_value, g, axis=1)})
+    _, o_mha = gpu_step(mha)
+    assert_decode_close(layouts.from_device(o_gqa, "bf16"), o64, "bf16", "gqa")
+    assert_decode_close(layouts.from_device(o_mha, "bf16"), o64, "bf16", "mha")
+
+
+def test_split_matches_unsplit():
+    b = layouts.scaled_config(4, max_seqs=1, max_len=2000)
+    _, _, o64 = oracle_step(b)
+    _, whole = gpu_step(b, partition=2048)
+    _, split = gpu_step(b, partition=16)
+    for name, o in (("whole", whole), ("split", split)):
+        assert_decode_close(layouts.from_device(o, "f16"), o64, "f16", name)
+    diff = (whole.float() - split.float()).abs().max().item()
+    assert diff <= 1e-3, diff
+
+
+def test_empty_context_gives_zeros():
+    b = layouts.make_paged_batch(num_q_heads=4, num_kv_heads=4, head_dim=64, dtype="f16",
+                                 block_size=16, context_lens=np.array([5, 40]), seed=6)
+    t = layouts.to_device(b)
+    t["context_lens"][0] = 0
+    out = ops.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                     b.scale, 40, partition=16)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0)
+    o64 = O.ref_decode(b.q[1:], b.k_cache, b.v_cache, b.block_tables[1:], b.context_lens[1:],
+                       b.scale, "f16")
+    assert_decode_close(layouts.from_device(out, "f16")[1:], o64, "f16", "after empty")
+
+
+def test_out_of_range_table_entry_is_caught_in_debug_mode(monkeypatch):
+    b = layouts.scaled_config(1)
+    t = layouts.to_device(b)
+    t["block_tables"][0, 1] = b.num_blocks + 5
+    monkeypatch.setenv("PA_DEBUG", "1")
+    with pytest.raises(ops.PagedAttentionError) as e:
+        ops.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                   b.scale, b.max_context_len)
+    assert e.value.code == 6
+    t["slot_mapping"][0] = b.num_blocks * b.block_size
+    with pytest.raises(ops.PagedAttentionError) as e:
+        ops.reshape_and_cache(t["new_key"], t["new_value"], t["k_cache"], t["v_cache"],
+                              t["slot_mapping"])
+    assert e.value.code == 6
