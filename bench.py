@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode step of paged attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+A step is the whole hot path over one batch: the cache write of the batch's
+new tokens (pa_reshape_and_cache), the partition kernel and the log-sum-exp
+reduce (pa_decode_partitions + pa_decode_reduce, which together are
+pa_decode). The default workload is the LLaMA-7B-layer MHA decode: 32
+sequences, 32/32 heads of dim 128, fp16, 16-token blocks, context lengths
+uniform in [128, 2048], scattered over a shuffled pool with 25% slack. Inputs
+are seeded synthetic data already resident in HBM.
+
+Timing: W untimed warm-up steps, then K timed steps. Before each timed step a
+1 GiB buffer is overwritten (outside the timed events) so the KV pools are not
+served from the 256 MB last-level cache; each step is bracketed by HIP events
+recorded on the stream the kernels run on, with events between its launches,
+so every kernel's duration is measured live. Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged-decode KV-read GB/s & % of HBM peak; decode tokens/sec at batch"
+KERNEL_SOURCES = ["paged_kv_cache_362_amd/csrc/pa_decode.hip",
+                  "paged_kv_cache_362_amd/csrc/pa_common.h",
+                  "paged_kv_cache_362_amd/csrc/pa_internal.h"]
+TRAFFIC_PROFILE = "profiles/pa_decode_partition_kernel.llama7b_mha_decode.pmc.md"
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--partition", type=int, default=0, help="tokens per partition (0=default)")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args(argv)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(config: int, partition: int):
+    """HBM bytes per partition-kernel launch from the committed counter profile.
+
+    Returns None unless the profile was taken on this workload with the
+    current kernel sources.
+    """
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if (rec.get("source_hash") != kernel_source_hash() or rec.get("config") != config
+            or rec.get("partition") != partition):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def calib_copy() -> None:
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
+
+
+def cpu_baseline(batch, seconds: float) -> dict:
+    """The float64 oracle on a bounded sample of the same batch, one thread."""
+    import numpy as np
+    import oracle.paged_attention as O
+    from paged_kv_cache_362_amd import sizing
+    import contextlib
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # threadpoolctl missing: numpy keeps its own thread count
+        limiter = contextlib.nullcontext()
+    done_bytes = 0
+    seqs_done = 0
+    with limiter:
+        t0 = time.perf_counter()
+        s = 0
+        while time.perf_counter() - t0 < seconds:
+            O.ref_decode(batch.q[s:s + 1], batch.k_cache, batch.v_cache,
+                         batch.block_tables[s:s + 1], batch.context_lens[s:s + 1], batch.scale,
+                         batch.dtype)
+            done_bytes += sizing.decode_algorithmic_bytes(
+                batch.context_lens[s:s + 1], batch.num_q_heads, batch.num_kv_heads,
+                batch.head_dim, batch.elem_bytes, batch.block_size)
+            seqs_done += 1
+            s = (s + 1) % batch.num_seqs
+        elapsed = time.perf_counter() - t0
+    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"float64 numpy oracle (ref_decode) over {seqs_done} sequences of this "
+                       f"workload taken in order (cycling), {elapsed:.1f} s on one host thread; "
+                       f"GB/s of the decode's algorithmic bytes"),
+            "seconds": round(elapsed, 2), "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(sequences or KV heads would shard across GPUs with no exchange inside "
+              f"attention, which is not built here)", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    if args.calib_copy:
+        calib_copy()
+        return 0
+
+    from paged_kv_cache_362_amd import layouts, ops, sizing
+    from paged_kv_cache_362_amd.layouts import CONFIGS
+
+    spec = CONFIGS[args.config]
+    t_gen = time.perf_counter()
+    b = layouts.make_config(args.config)
+    gen_s = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t = layouts.to_device(b, dev)
+    s, hq, hkv, d = b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim
+    tdtype = t["q"].dtype
+    part = ops.partition_size(s, hq, hkv, d, b.max_context_len, tdtype, args.partition)
+    ws_bytes = ops.workspace_size(s, hq, hkv, d, b.max_context_len, tdtype, part)
+    out = torch.empty_like(t["q"])
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        ops.reshape_and_cache(t["new_key"], t["new_value"], t["k_cache"], t["v_cache"],
+                              t["slot_mapping"])
+        if ev is not None:
+            ev[1].record()
+        ops.decode_partitions(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                              t["context_lens"], b.scale, b.max_context_len, out, ws, part)
+        if ev is not None:
+            ev[2].record()
+        ops.decode_reduce(out, t["context_lens"], hkv, b.max_context_len, ws, part)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        if flush is not None:
+            flush.zero_()
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.zero_()
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in events])
+    cache_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    part_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    red_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
+
+    e = b.elem_bytes
+    lens = b.context_lens
+    decode_bytes = sizing.decode_algorithmic_bytes(lens, hq, hkv, d, e, b.block_size)
+    cache_bytes = sizing.reshape_and_cache_bytes(b.slot_mapping.shape[0], hkv, d, e)
+    step_bytes = decode_bytes + cache_bytes
+    # the partition kernel moves everything but the output rows the reduce writes
+    part_bytes = decode_bytes - s * hq * d * e
+    kv_bytes = sizing.kv_read_bytes(lens, hkv, d, e)
+    ms = float(step_ms.mean())
+    value = step_bytes / (ms * 1e-3) / 1e9
+    achieved = part_bytes / (float(part_ms.mean()) * 1e-3) / 1e9
+
+    traffic = stored_traffic(args.config, part)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": b.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": spec.name, "config": args.config, "num_seqs": s, "num_q_heads": hq,
+            "num_kv_heads": hkv, "head_dim": d, "block_size": b.block_size,
+            "context_tokens": int(lens.sum()), "max_context_len": b.max_context_len,
+            "num_blocks": b.num_blocks, "partition_size": part, "parallelism": "none (1 GPU)",
+            "cache_flush_between_steps": flush is not None,
+        },
+        "pct_hbm_peak": round(100 * value / sizing.HBM_PEAK_GBPS, 2),
+        "tokens_per_s": round(s / (ms * 1e-3), 1),
+        "kv_read_GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
+        "kernel_ms": {"reshape_and_cache": round(float(cache_ms.mean()), 5),
+                      "decode_partition": round(float(part_ms.mean()), 5),
+                      "decode_reduce": round(float(red_ms.mean()), 5),
+                      "step_median": round(float(np.median(step_ms)), 5),
+                      "step_min": round(float(step_ms.min()), 5)},
+        "bytes_per_step": {"algorithmic": int(step_bytes), "decode": int(decode_bytes),
+                           "partition_kernel": int(part_bytes), "kv": int(kv_bytes)},
+        "wall_s_timed_loop": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": sizing.HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / sizing.HBM_PEAK_GBPS, 4),
+                     "kernel": "decode_partition_kernel",
+                     "traffic": traffic},
+        "input_gen_s": round(gen_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

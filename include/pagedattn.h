@@ -153,6 +153,38 @@ int32_t pa_decode(void *out, const void *q, const void *k_cache,
                   int32_t partition_size, int32_t dtype, void *workspace,
                   size_t workspace_bytes, void *stream);
 
+/*
+ * pa_decode_partitions / pa_decode_reduce - the two launches of pa_decode,
+ * callable separately (pa_decode is exactly one followed by the other on the
+ * same stream).
+ *
+ * pa_decode_partitions takes pa_decode's arguments and runs the partition
+ * kernel only: sequences that fit in one partition get their output rows;
+ * the others leave per-partition (max, sum, weighted values) in `workspace`.
+ *
+ * pa_decode_reduce then combines those partials into the remaining output
+ * rows (log-sum-exp combine, [INFRA] Q2 of §8). Its size arguments must equal
+ * the ones given to pa_decode_partitions; `workspace` must hold that call's
+ * partials. With a single partition (workspace size 0) it enqueues nothing.
+ */
+int32_t pa_decode_partitions(void *out, const void *q, const void *k_cache,
+                             const void *v_cache, const int32_t *block_tables,
+                             const int32_t *context_lens, float scale,
+                             int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int32_t num_blocks,
+                             int32_t max_blocks_per_seq,
+                             int32_t max_context_len, int32_t partition_size,
+                             int32_t dtype, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+int32_t pa_decode_reduce(void *out, const int32_t *context_lens,
+                         int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim,
+                         int32_t max_context_len, int32_t partition_size,
+                         int32_t dtype, const void *workspace,
+                         size_t workspace_bytes, void *stream);
+
 /* A static, human-readable name of a status code. */
 const char *pa_status_str(int32_t status);
 

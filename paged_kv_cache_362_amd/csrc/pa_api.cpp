@@ -160,12 +160,19 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
                              num_partitions(max_context_len, part));
 }
 
-int32_t pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
-                  const int32_t *block_tables, const int32_t *context_lens, float scale,
-                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                  int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size,
-                  int32_t dtype, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by pa_decode and pa_decode_partitions; fills `p`.
+int32_t prepare_decode(pa::DecodeParams &p, void *out, const void *q, const void *k_cache,
+                       const void *v_cache, const int32_t *block_tables,
+                       const int32_t *context_lens, float scale, int32_t num_seqs,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                       int32_t max_context_len, int32_t partition_size, int32_t dtype,
+                       void *workspace, size_t workspace_bytes, hipStream_t s, bool *no_work) {
+  *no_work = false;
   int32_t st = check_decode_shapes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                    max_context_len, dtype);
   if (st != PA_OK) return st;
@@ -176,7 +183,10 @@ int32_t pa_decode(void *out, const void *q, const void *k_cache, const void *v_c
     return PA_ERR_BAD_SHAPE;
   const int32_t part = resolve_partition(partition_size);
   if (part < 0) return PA_ERR_BAD_SHAPE;
-  if (num_seqs == 0) return PA_OK;
+  if (num_seqs == 0) {
+    *no_work = true;
+    return PA_OK;
+  }
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return PA_ERR_NULL_POINTER;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
@@ -187,7 +197,6 @@ int32_t pa_decode(void *out, const void *q, const void *k_cache, const void *v_c
     if (workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
     if (!aligned16(workspace)) return PA_ERR_UNSUPPORTED;
   }
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   if (debug_checks()) {
     std::vector<int32_t> lens(num_seqs);
@@ -207,7 +216,7 @@ int32_t pa_decode(void *out, const void *q, const void *k_cache, const void *v_c
     }
   }
 
-  pa::DecodeParams p{};
+  p = pa::DecodeParams{};
   p.out = out;
   if (need > 0) {
     const size_t rows = size_t(num_seqs) * num_q_heads * max_parts;
@@ -233,7 +242,92 @@ int32_t pa_decode(void *out, const void *q, const void *k_cache, const void *v_c
   p.partition_size = part;
   p.max_partitions = max_parts;
   p.dtype = dtype;
-  return pa::launch_decode(p, s) == hipSuccess ? PA_OK : PA_ERR_HIP;
+  return PA_OK;
+}
+
+int32_t decode_stage(pa::DecodeStage stage, void *out, const void *q, const void *k_cache,
+                     const void *v_cache, const int32_t *block_tables,
+                     const int32_t *context_lens, float scale, int32_t num_seqs,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                     int32_t max_context_len, int32_t partition_size, int32_t dtype,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  pa::DecodeParams p;
+  bool no_work = false;
+  const int32_t st = prepare_decode(p, out, q, k_cache, v_cache, block_tables, context_lens,
+                                    scale, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                    block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                                    partition_size, dtype, workspace, workspace_bytes, s,
+                                    &no_work);
+  if (st != PA_OK || no_work) return st;
+  return pa::launch_decode(p, s, stage) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                  const int32_t *block_tables, const int32_t *context_lens, float scale,
+                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                  int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size,
+                  int32_t dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_stage(pa::kStageBoth, out, q, k_cache, v_cache, block_tables, context_lens,
+                      scale, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                      num_blocks, max_blocks_per_seq, max_context_len, partition_size, dtype,
+                      workspace, workspace_bytes, stream);
+}
+
+int32_t pa_decode_partitions(void *out, const void *q, const void *k_cache, const void *v_cache,
+                             const int32_t *block_tables, const int32_t *context_lens,
+                             float scale, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t max_blocks_per_seq,
+                             int32_t max_context_len, int32_t partition_size, int32_t dtype,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_stage(pa::kStagePartitions, out, q, k_cache, v_cache, block_tables,
+                      context_lens, scale, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                      block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                      partition_size, dtype, workspace, workspace_bytes, stream);
+}
+
+int32_t pa_decode_reduce(void *out, const int32_t *context_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t max_context_len, int32_t partition_size, int32_t dtype,
+                         const void *workspace, size_t workspace_bytes, void *stream) {
+  int32_t st = check_decode_shapes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                   max_context_len, dtype);
+  if (st != PA_OK) return st;
+  const int32_t part = resolve_partition(partition_size);
+  if (part < 0) return PA_ERR_BAD_SHAPE;
+  const int32_t max_parts = num_partitions(max_context_len, part);
+  const size_t need = workspace_bytes_for(num_seqs, num_q_heads, head_dim, max_parts);
+  if (num_seqs == 0 || need == 0) return PA_OK;
+  if (!out || !context_lens || !workspace) return PA_ERR_NULL_POINTER;
+  if (workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(workspace)) return PA_ERR_UNSUPPORTED;
+  pa::DecodeParams p{};
+  const size_t rows = size_t(num_seqs) * num_q_heads * max_parts;
+  float *ws = static_cast<float *>(const_cast<void *>(workspace));
+  p.out = out;
+  p.ws_acc = ws;
+  p.ws_m = ws + rows * head_dim;
+  p.ws_l = p.ws_m + rows;
+  p.context_lens = context_lens;
+  p.num_seqs = num_seqs;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_q_heads / num_kv_heads;
+  p.head_dim = head_dim;
+  p.max_context_len = max_context_len;
+  p.partition_size = part;
+  p.max_partitions = max_parts;
+  p.dtype = dtype;
+  return pa::launch_decode(p, reinterpret_cast<hipStream_t>(stream), pa::kStageReduce) ==
+                 hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -300,42 +300,47 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeParams p) {
 }
 
 template <int DT, int D, int G>
-static hipError_t launch_dtg(const DecodeParams &p, hipStream_t stream) {
-  dim3 grid(p.max_partitions, p.num_kv_heads, p.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, G>), grid, dim3(kThreads), 0, stream, p);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || p.max_partitions <= 1) return err;
-  dim3 rgrid(p.num_kv_heads * G, p.num_seqs);
-  hipLaunchKernelGGL((decode_reduce_kernel<DT, D>), rgrid, dim3(D), 0, stream, p);
-  return hipGetLastError();
+static hipError_t launch_dtg(const DecodeParams &p, hipStream_t stream, DecodeStage stage) {
+  if (stage != kStageReduce) {
+    dim3 grid(p.max_partitions, p.num_kv_heads, p.num_seqs);
+    hipLaunchKernelGGL((decode_partition_kernel<DT, D, G>), grid, dim3(kThreads), 0, stream, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (stage != kStagePartitions && p.max_partitions > 1) {
+    dim3 rgrid(p.num_kv_heads * G, p.num_seqs);
+    hipLaunchKernelGGL((decode_reduce_kernel<DT, D>), rgrid, dim3(D), 0, stream, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 template <int DT, int D>
-static hipError_t launch_dt(const DecodeParams &p, hipStream_t stream) {
+static hipError_t launch_dt(const DecodeParams &p, hipStream_t stream, DecodeStage stage) {
   switch (p.group) {
-    case 1: return launch_dtg<DT, D, 1>(p, stream);
-    case 2: return launch_dtg<DT, D, 2>(p, stream);
-    case 4: return launch_dtg<DT, D, 4>(p, stream);
-    case 8: return launch_dtg<DT, D, 8>(p, stream);
+    case 1: return launch_dtg<DT, D, 1>(p, stream, stage);
+    case 2: return launch_dtg<DT, D, 2>(p, stream, stage);
+    case 4: return launch_dtg<DT, D, 4>(p, stream, stage);
+    case 8: return launch_dtg<DT, D, 8>(p, stream, stage);
   }
   return hipErrorInvalidValue;
 }
 
 template <int DT>
-static hipError_t launch_d(const DecodeParams &p, hipStream_t stream) {
+static hipError_t launch_d(const DecodeParams &p, hipStream_t stream, DecodeStage stage) {
   switch (p.head_dim) {
-    case 64: return launch_dt<DT, 64>(p, stream);
-    case 128: return launch_dt<DT, 128>(p, stream);
-    case 256: return launch_dt<DT, 256>(p, stream);
+    case 64: return launch_dt<DT, 64>(p, stream, stage);
+    case 128: return launch_dt<DT, 128>(p, stream, stage);
+    case 256: return launch_dt<DT, 256>(p, stream, stage);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode(const DecodeParams &p, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams &p, hipStream_t stream, DecodeStage stage) {
   switch (p.dtype) {
-    case PA_F32: return launch_d<PA_F32>(p, stream);
-    case PA_F16: return launch_d<PA_F16>(p, stream);
-    case PA_BF16: return launch_d<PA_BF16>(p, stream);
+    case PA_F32: return launch_d<PA_F32>(p, stream, stage);
+    case PA_F16: return launch_d<PA_F16>(p, stream, stage);
+    case PA_BF16: return launch_d<PA_BF16>(p, stream, stage);
   }
   return hipErrorInvalidValue;
 }

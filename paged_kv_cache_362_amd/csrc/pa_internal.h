@@ -48,7 +48,9 @@ struct CacheParams {
   int64_t num_slots;  // num_blocks * block_size
 };
 
-hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
+enum DecodeStage { kStageBoth = 0, kStagePartitions = 1, kStageReduce = 2 };
+
+hipError_t launch_decode(const DecodeParams &p, hipStream_t stream, DecodeStage stage);
 hipError_t launch_reshape_and_cache(const CacheParams &p, hipStream_t stream);
 
 }  // namespace pa

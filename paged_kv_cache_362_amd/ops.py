@@ -92,16 +92,8 @@ def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim:
     return size
 
 
-def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
-           max_context_len: int, out: torch.Tensor | None = None,
-           workspace: torch.Tensor | None = None, partition: int = 0) -> torch.Tensor:
-    """Paged decode attention; returns out [S, Hq, D] in q's dtype.
-
-    ``max_context_len`` is the host-side maximum of ``context_lens``.
-    ``workspace`` (uint8, at least ``workspace_size(...)`` bytes) is allocated
-    here when not given.
-    """
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, out,
+                 workspace, partition):
     _on_gpu(q, k_cache, v_cache, block_tables, context_lens)
     _require(q.dim() == 3, "q must be [S, Hq, D]")
     _require(k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "pools must be [N, Hkv, B, D]")
@@ -111,7 +103,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     _require(context_lens.dtype == torch.int32 and context_lens.shape == (q.shape[0],),
              "context_lens must be int32 [S]")
     s, hq, d = q.shape
-    n, hkv, bs, d2 = k_cache.shape
+    _, hkv, _, d2 = k_cache.shape
     _require(d == d2 and block_tables.shape[0] == s, "inconsistent shapes")
     if out is None:
         out = torch.empty_like(q)
@@ -123,10 +115,55 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     else:
         _on_gpu(workspace)
-    code = lib().pa_decode(
-        _dev_ptr(out), _dev_ptr(q), _dev_ptr(k_cache), _dev_ptr(v_cache),
-        _dev_ptr(block_tables), _dev_ptr(context_lens), float(scale), s, hq, hkv, d, bs, n,
-        block_tables.shape[1], int(max_context_len), int(partition), dtype_code(q.dtype),
-        _dev_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
-    _check("pa_decode", code)
+    return out, workspace
+
+
+def _launch_decode(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale,
+                   max_context_len, out, workspace, partition):
+    s, hq, d = q.shape
+    n, hkv, bs, _ = k_cache.shape
+    fn = getattr(lib(), fn_name)
+    code = fn(_dev_ptr(out), _dev_ptr(q), _dev_ptr(k_cache), _dev_ptr(v_cache),
+              _dev_ptr(block_tables), _dev_ptr(context_lens), float(scale), s, hq, hkv, d, bs, n,
+              block_tables.shape[1], int(max_context_len), int(partition), dtype_code(q.dtype),
+              _dev_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
+    _check(fn_name, code)
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+           max_context_len: int, out: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None, partition: int = 0) -> torch.Tensor:
+    """Paged decode attention; returns out [S, Hq, D] in q's dtype.
+
+    ``max_context_len`` is the host-side maximum of ``context_lens``.
+    ``workspace`` (uint8, at least ``workspace_size(...)`` bytes) is allocated
+    here when not given.
+    """
+    out, workspace = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                  max_context_len, out, workspace, partition)
+    _launch_decode("pa_decode", q, k_cache, v_cache, block_tables, context_lens, scale,
+                   max_context_len, out, workspace, partition)
     return out
+
+
+def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale,
+                      max_context_len, out, workspace, partition: int = 0) -> None:
+    """First launch of ``decode`` (partition kernel); ``out``/``workspace`` are required."""
+    _require(out is not None and workspace is not None, "out and workspace are required")
+    _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, out,
+                 workspace, partition)
+    _launch_decode("pa_decode_partitions", q, k_cache, v_cache, block_tables, context_lens,
+                   scale, max_context_len, out, workspace, partition)
+
+
+def decode_reduce(out, context_lens, num_kv_heads: int, max_context_len: int, workspace,
+                  partition: int = 0) -> None:
+    """Second launch of ``decode``: combine the partitions left in ``workspace``."""
+    _on_gpu(out, context_lens, workspace)
+    s, hq, d = out.shape
+    code = lib().pa_decode_reduce(
+        _dev_ptr(out), _dev_ptr(context_lens), s, hq, num_kv_heads, d, int(max_context_len),
+        int(partition), dtype_code(out.dtype), _dev_ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(out))
+    _check("pa_decode_reduce", code)

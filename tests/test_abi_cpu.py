@@ -32,8 +32,9 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("pa_reshape_and_cache", "pa_decode", "pa_decode_workspace_size",
-              "pa_decode_partition_size", "pa_status_str", "pa_abi_version"):
+    for n in ("pa_reshape_and_cache", "pa_decode", "pa_decode_partitions", "pa_decode_reduce",
+              "pa_decode_workspace_size", "pa_decode_partition_size", "pa_status_str",
+              "pa_abi_version"):
         assert n in names
 
 
@@ -106,3 +107,23 @@ def test_cache_write_rejects_bad_arguments_before_launch(lib):
     assert f(16, 16, 16, 16, 16, 1, 4, 64, 24, 8, F16, None) == UNSUP
     assert f(16, 16, 24, 16, 16, 1, 4, 64, 16, 8, F16, None) == UNSUP
     assert f(None, None, None, None, None, 0, 4, 64, 16, 8, F16, None) == OK
+
+
+def test_reduce_rejects_bad_arguments_before_launch(lib):
+    f = lib.pa_decode_reduce
+    # single partition: nothing to combine, nothing enqueued
+    assert f(16, 16, 1, 4, 4, 64, 50, 0, F16, None, 0, None) == OK
+    assert f(16, None, 1, 4, 4, 64, 600, 0, F16, 16, 1 << 20, None) == NULLP
+    assert f(16, 16, 1, 4, 4, 64, 600, 0, F16, 16, 10, None) == WS
+    assert f(16, 16, 1, 6, 4, 64, 600, 0, F16, 16, 1 << 20, None) == SHAPE
+    assert f(16, 16, 1, 4, 4, 64, 600, 8, F16, 16, 1 << 20, None) == SHAPE
+
+
+def test_partitions_entry_validates_like_decode(lib):
+    a = [16] * 6 + [0.125, 1, 4, 4, 64, 16, 4, 4, 50, 0, F32, None, 0, None]
+    bad = list(a)
+    bad[1] = None
+    assert lib.pa_decode_partitions(*bad) == NULLP
+    bad = list(a)
+    bad[14] = 65
+    assert lib.pa_decode_partitions(*bad) == SHAPE

@@ -281,3 +281,18 @@ def test_out_of_range_table_entry_is_caught_in_debug_mode(monkeypatch):
         ops.reshape_and_cache(t["new_key"], t["new_value"], t["k_cache"], t["v_cache"],
                               t["slot_mapping"])
     assert e.value.code == 6
+
+
+def test_two_launch_split_equals_decode():
+    """pa_decode_partitions then pa_decode_reduce is pa_decode, bit for bit."""
+    b = layouts.scaled_config(2, max_seqs=4, max_len=700)
+    t, whole = gpu_step(b, partition=64)
+    out = torch.empty_like(t["q"])
+    ws = torch.empty(ops.workspace_size(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                        b.max_context_len, t["q"].dtype, 64),
+                     dtype=torch.uint8, device="cuda")
+    ops.decode_partitions(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                          t["context_lens"], b.scale, b.max_context_len, out, ws, 64)
+    ops.decode_reduce(out, t["context_lens"], b.num_kv_heads, b.max_context_len, ws, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), whole.view(torch.int16))
