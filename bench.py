@@ -4,18 +4,18 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
 
 A step is the whole hot path over one batch: the cache write of the batch's
-new tokens (pa_reshape_and_cache), the partition kernel and the log-sum-exp
-reduce (pa_decode_partitions + pa_decode_reduce, which together are
-pa_decode). The default workload is the LLaMA-7B-layer MHA decode: 32
-sequences, 32/32 heads of dim 128, fp16, 16-token blocks, context lengths
-uniform in [128, 2048], scattered over a shuffled pool with 25% slack. Inputs
-are seeded synthetic data already resident in HBM.
+new tokens (pa_reshape_and_cache) and the decode (pa_decode, balanced form: a
+single launch that also combines split heads). The default workload is the
+LLaMA-7B-layer MHA decode: 32 sequences, 32/32 heads of dim 128, fp16, 16-token
+blocks, context lengths uniform in [128, 2048], scattered over a shuffled pool
+with 25% slack. Inputs are seeded synthetic data already resident in HBM.
 
-Timing: W untimed warm-up steps, then K timed steps. Before each timed step a
-1 GiB buffer is overwritten (outside the timed events) so the KV pools are not
-served from the 256 MB last-level cache; each step is bracketed by HIP events
-recorded on the stream the kernels run on, with events between its launches,
-so every kernel's duration is measured live. Prints one JSON line.
+Timing: W untimed warm-up steps, then K timed steps. Before each step a 1 GiB
+buffer is read (outside the timed events) so the KV pools are not served from
+the 256 MB last-level cache; a read leaves no dirty lines behind, so the step
+is not charged for writing back the flush. Each step is bracketed by HIP events
+recorded on the stream the kernels run on, with an event between its two
+launches, so each kernel's duration is measured live. Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -35,7 +35,7 @@ METRIC = "paged-decode KV-read GB/s & % of HBM peak; decode tokens/sec at batch"
 KERNEL_SOURCES = ["paged_kv_cache_362_amd/csrc/pa_decode.hip",
                   "paged_kv_cache_362_amd/csrc/pa_common.h",
                   "paged_kv_cache_362_amd/csrc/pa_internal.h"]
-TRAFFIC_PROFILE = "profiles/pa_decode_partition_kernel.llama7b_mha_decode.pmc.md"
+TRAFFIC_PROFILE = "profiles/decode_flat_kernel.llama7b_mha_decode.pmc.md"
 
 
 def parse_args(argv=None):
@@ -45,7 +45,8 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--partition", type=int, default=0, help="tokens per partition (0=default)")
+    ap.add_argument("--partition", type=int, default=0,
+                    help="0 = balanced single launch (default); >0 = fixed partitions")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -152,11 +153,10 @@ def main(argv=None) -> int:
     t = layouts.to_device(b, dev)
     s, hq, hkv, d = b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim
     tdtype = t["q"].dtype
-    part = ops.partition_size(s, hq, hkv, d, b.max_context_len, tdtype, args.partition)
-    ws_bytes = ops.workspace_size(s, hq, hkv, d, b.max_context_len, tdtype, part)
+    part = args.partition
     out = torch.empty_like(t["q"])
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    ws = ops.new_workspace(s, hq, hkv, d, b.max_context_len, tdtype, dev, part)
+    flush = None if args.no_flush else torch.ones(1 << 28, dtype=torch.float32, device=dev)
 
     def step(ev=None):
         if ev is not None:
@@ -165,46 +165,40 @@ def main(argv=None) -> int:
                               t["slot_mapping"])
         if ev is not None:
             ev[1].record()
-        ops.decode_partitions(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
-                              t["context_lens"], b.scale, b.max_context_len, out, ws, part)
+        ops.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                   b.scale, b.max_context_len, out, ws, part)
         if ev is not None:
             ev[2].record()
-        ops.decode_reduce(out, t["context_lens"], hkv, b.max_context_len, ws, part)
-        if ev is not None:
-            ev[3].record()
 
     for _ in range(args.warmup):
         if flush is not None:
-            flush.zero_()
+            flush.amax()
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.steps):
         if flush is not None:
-            flush.zero_()
+            flush.amax()
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
-    step_ms = np.array([e[0].elapsed_time(e[3]) for e in events])
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in events])
     cache_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    part_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
-    red_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
 
     e = b.elem_bytes
     lens = b.context_lens
     decode_bytes = sizing.decode_algorithmic_bytes(lens, hq, hkv, d, e, b.block_size)
     cache_bytes = sizing.reshape_and_cache_bytes(b.slot_mapping.shape[0], hkv, d, e)
     step_bytes = decode_bytes + cache_bytes
-    # the partition kernel moves everything but the output rows the reduce writes
-    part_bytes = decode_bytes - s * hq * d * e
     kv_bytes = sizing.kv_read_bytes(lens, hkv, d, e)
     ms = float(step_ms.mean())
     value = step_bytes / (ms * 1e-3) / 1e9
-    achieved = part_bytes / (float(part_ms.mean()) * 1e-3) / 1e9
+    achieved = decode_bytes / (float(dec_ms.mean()) * 1e-3) / 1e9
 
     traffic = stored_traffic(args.config, part)
     line = {
@@ -224,24 +218,26 @@ def main(argv=None) -> int:
             "workload": spec.name, "config": args.config, "num_seqs": s, "num_q_heads": hq,
             "num_kv_heads": hkv, "head_dim": d, "block_size": b.block_size,
             "context_tokens": int(lens.sum()), "max_context_len": b.max_context_len,
-            "num_blocks": b.num_blocks, "partition_size": part, "parallelism": "none (1 GPU)",
+            "num_blocks": b.num_blocks,
+            "decode_form": "balanced" if part == 0 else f"fixed partitions of {part}",
+            "parallelism": "none (1 GPU)",
             "cache_flush_between_steps": flush is not None,
         },
         "pct_hbm_peak": round(100 * value / sizing.HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(s / (ms * 1e-3), 1),
         "kv_read_GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
         "kernel_ms": {"reshape_and_cache": round(float(cache_ms.mean()), 5),
-                      "decode_partition": round(float(part_ms.mean()), 5),
-                      "decode_reduce": round(float(red_ms.mean()), 5),
+                      "decode": round(float(dec_ms.mean()), 5),
+                      "decode_median": round(float(np.median(dec_ms)), 5),
                       "step_median": round(float(np.median(step_ms)), 5),
                       "step_min": round(float(step_ms.min()), 5)},
         "bytes_per_step": {"algorithmic": int(step_bytes), "decode": int(decode_bytes),
-                           "partition_kernel": int(part_bytes), "kv": int(kv_bytes)},
+                           "kv": int(kv_bytes)},
         "wall_s_timed_loop": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2),
                      "peak": sizing.HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / sizing.HBM_PEAK_GBPS, 4),
-                     "kernel": "decode_partition_kernel",
+                     "kernel": "decode_flat_kernel" if part == 0 else "decode_partition_kernel",
                      "traffic": traffic},
         "input_gen_s": round(gen_s, 2),
     }

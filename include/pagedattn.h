@@ -48,11 +48,15 @@
  * Errors: arguments are checked on the host before anything is enqueued; on a
  * non-zero status nothing was enqueued (except PA_ERR_HIP, which reports a
  * launch failure). Values that live in device memory (table entries in
- * [0, num_blocks), 1 <= context_lens[s] <= max_context_len, distinct slots)
- * are preconditions; they are checked only when the environment variable
- * PA_DEBUG is set to a non-zero value, in which case the call copies them to
- * the host (synchronising the stream) and returns PA_ERR_BAD_INDEX on a
- * violation. A context length of 0 yields an all-zero output row.
+ * [0, num_blocks), 1 <= context_lens[s] <= max_context_len, distinct slots,
+ * zero arrival counters) are preconditions; they are checked only when the
+ * environment variable PA_DEBUG is set to a non-zero value, in which case the
+ * call copies them to the host (synchronising the stream) and returns
+ * PA_ERR_BAD_INDEX on a violation. A context length of 0 yields an all-zero
+ * output row.
+ *
+ * Tuning: PA_FLAT_WGS_PER_CU (a positive integer) overrides the number of
+ * workgroups per compute unit of the balanced form (default: as many as fit).
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -99,29 +103,18 @@ int32_t pa_reshape_and_cache(const void *key, const void *value, void *k_cache,
 /*
  * pa_decode_workspace_size - device scratch bytes pa_decode needs.
  *
- * The context of each sequence is cut into partitions of `partition_size`
- * tokens (0 = the library's default for these shapes); each partition is
- * processed by its own workgroup and, when a sequence has more than one,
- * the partial results are combined by a log-sum-exp reduction (split-K in the
- * manner of flash decoding, [INFRA] Q2 of §8). Returns 0 when max_context_len
- * fits in one partition, and (size_t)-1 for arguments pa_decode would reject.
+ * partition_size selects the form of the decode (see pa_decode): 0 for the
+ * balanced single launch, or a fixed partition size. Returns (size_t)-1 for
+ * arguments pa_decode would reject. The workspace starts with one int32
+ * arrival counter per (sequence, KV head); the balanced form needs them to be
+ * zero when a call starts and leaves them zero when it ends, so a workspace
+ * must be zero-filled once, before its first use. The fixed-partition form
+ * never touches the counters, so one workspace may serve both forms.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                 int32_t num_kv_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t partition_size,
                                 int32_t dtype);
-
-/*
- * pa_decode_partition_size - the partition size pa_decode will use.
- *
- * `requested` = 0 picks the library default for the shapes; otherwise it must
- * be a positive multiple of 16 and is returned unchanged. Returns -1 for
- * arguments pa_decode would reject.
- */
-int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
-                                 int32_t num_kv_heads, int32_t head_dim,
-                                 int32_t max_context_len, int32_t requested,
-                                 int32_t dtype);
 
 /*
  * pa_decode - one decode step of paged attention.
@@ -130,19 +123,34 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads,
  * where K_s and V_s are the first context_lens[s] rows of KV head
  * h / (num_q_heads / num_kv_heads), gathered through block_tables[s].
  * Accumulation is float32; out is rounded once to `dtype` (nearest even).
- * Slots past a sequence's context and table entries past its last block are
- * never read.
+ * Table entries past a sequence's last block are never used, and slots past
+ * its context never contribute (entries are clamped into the pool, so no read
+ * leaves it).
+ *
+ * The context is processed in pieces whose partial results are combined by a
+ * log-sum-exp reduction (split-K in the manner of flash decoding, [INFRA] Q2
+ * of §8). partition_size chooses how it is cut:
+ *   0     balanced form (the default): one launch whose workgroups each take an
+ *         equal share of all (sequence, KV head, 16-token tile) work, however
+ *         unequal the context lengths; a (sequence, KV head) split between
+ *         workgroups is combined by the last of them to finish. Used for
+ *         num_seqs <= 4096; beyond that the call falls back to fixed
+ *         partitions of 256 tokens.
+ *   P > 0 fixed partitions of P tokens (a multiple of 16, at most 4096): one
+ *         workgroup per (partition, KV head, sequence), then a second launch
+ *         combines the partitions.
  *
  * scale            the softmax scale (1/sqrt(head_dim) for standard attention)
- * max_context_len  max over s of context_lens[s] (host value: sizes the grid)
- * partition_size   0 = default, else a multiple of 16 (see above)
+ * max_context_len  max over s of context_lens[s] (host value)
  * workspace        device scratch of at least pa_decode_workspace_size(...)
- *                  bytes (may be NULL when that size is 0); its contents on
- *                  entry do not matter
+ *                  bytes, zero-filled before its first use (see above); it
+ *                  may be NULL only for the fixed form with max_context_len
+ *                  <= partition_size (nothing to combine)
  *
- * Supported: head_dim in {64, 128, 256}; block_size in {8, 16, 32, 64};
- * num_q_heads / num_kv_heads in {1, 2, 4, 8}; dtype in {PA_F32, PA_F16,
- * PA_BF16}; max_context_len <= max_blocks_per_seq * block_size.
+ * Supported: head_dim in {64, 128, 256} (rows of at most 512 bytes, so not
+ * 256 with PA_F32); block_size in {8, 16, 32, 64}; num_q_heads / num_kv_heads
+ * in {1, 2, 4, 8}; dtype in {PA_F32, PA_F16, PA_BF16}; max_context_len <=
+ * max_blocks_per_seq * block_size.
  */
 int32_t pa_decode(void *out, const void *q, const void *k_cache,
                   const void *v_cache, const int32_t *block_tables,
@@ -152,38 +160,6 @@ int32_t pa_decode(void *out, const void *q, const void *k_cache,
                   int32_t max_blocks_per_seq, int32_t max_context_len,
                   int32_t partition_size, int32_t dtype, void *workspace,
                   size_t workspace_bytes, void *stream);
-
-/*
- * pa_decode_partitions / pa_decode_reduce - the two launches of pa_decode,
- * callable separately (pa_decode is exactly one followed by the other on the
- * same stream).
- *
- * pa_decode_partitions takes pa_decode's arguments and runs the partition
- * kernel only: sequences that fit in one partition get their output rows;
- * the others leave per-partition (max, sum, weighted values) in `workspace`.
- *
- * pa_decode_reduce then combines those partials into the remaining output
- * rows (log-sum-exp combine, [INFRA] Q2 of §8). Its size arguments must equal
- * the ones given to pa_decode_partitions; `workspace` must hold that call's
- * partials. With a single partition (workspace size 0) it enqueues nothing.
- */
-int32_t pa_decode_partitions(void *out, const void *q, const void *k_cache,
-                             const void *v_cache, const int32_t *block_tables,
-                             const int32_t *context_lens, float scale,
-                             int32_t num_seqs, int32_t num_q_heads,
-                             int32_t num_kv_heads, int32_t head_dim,
-                             int32_t block_size, int32_t num_blocks,
-                             int32_t max_blocks_per_seq,
-                             int32_t max_context_len, int32_t partition_size,
-                             int32_t dtype, void *workspace,
-                             size_t workspace_bytes, void *stream);
-
-int32_t pa_decode_reduce(void *out, const int32_t *context_lens,
-                         int32_t num_seqs, int32_t num_q_heads,
-                         int32_t num_kv_heads, int32_t head_dim,
-                         int32_t max_context_len, int32_t partition_size,
-                         int32_t dtype, const void *workspace,
-                         size_t workspace_bytes, void *stream);
 
 /* A static, human-readable name of a status code. */
 const char *pa_status_str(int32_t status);

@@ -21,13 +21,8 @@ SIGNATURES = {
     "pa_reshape_and_cache": (_i32, [_ptr, _ptr, _ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _ptr]),
     "pa_decode_workspace_size": (_size, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
-    "pa_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _f32, _i32, _i32, _i32, _i32, _i32,
                          _i32, _i32, _i32, _i32, _i32, _ptr, _size, _ptr]),
-    "pa_decode_partitions": (_i32, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _f32, _i32, _i32, _i32,
-                                    _i32, _i32, _i32, _i32, _i32, _i32, _i32, _ptr, _size, _ptr]),
-    "pa_decode_reduce": (_i32, [_ptr, _ptr, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _ptr,
-                                _size, _ptr]),
     "pa_status_str": (ctypes.c_char_p, [_i32]),
     "pa_abi_version": (_i32, []),
 }

@@ -1,12 +1,15 @@
-// pa_api.cpp - the C ABI of libpagedattn.so: argument checks, the partition
-// policy, workspace sizing and the optional (PA_DEBUG) device-side checks.
-// Declarations and the contract of every entry point are in
-// include/pagedattn.h.
+// pa_api.cpp - the C ABI of libpagedattn.so: argument checks, the choice of
+// decode form, workspace layout and sizing, the launch grid of the balanced
+// form, and the optional (PA_DEBUG) device-side checks. Declarations and the
+// contract of every entry point are in include/pagedattn.h.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
 #include <unordered_set>
 #include <vector>
 
@@ -15,7 +18,8 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
+constexpr size_t kAlign = 256;
 
 bool debug_checks() {
   const char *e = std::getenv("PA_DEBUG");
@@ -42,8 +46,9 @@ bool head_dim_ok(int32_t d) { return d == 64 || d == 128 || d == 256; }
 bool block_size_ok(int32_t b) { return b == 8 || b == 16 || b == 32 || b == 64; }
 bool group_ok(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Shape checks shared by pa_decode and its sizing helpers.
+// Shape checks shared by pa_decode and pa_decode_workspace_size.
 int32_t check_decode_shapes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t max_context_len, int32_t dtype) {
   if (num_seqs < 0 || num_seqs > 65535 || num_kv_heads <= 0 || num_kv_heads > 65535 ||
@@ -52,13 +57,14 @@ int32_t check_decode_shapes(int32_t num_seqs, int32_t num_q_heads, int32_t num_k
   if (num_q_heads % num_kv_heads != 0) return PA_ERR_BAD_SHAPE;
   if (elem_bytes(dtype) == 0 || !head_dim_ok(head_dim) || !group_ok(num_q_heads / num_kv_heads))
     return PA_ERR_UNSUPPORTED;
+  if (head_dim * elem_bytes(dtype) > 512) return PA_ERR_UNSUPPORTED;  // f32 rows of 256
   return PA_OK;
 }
 
-int32_t resolve_partition(int32_t requested) {
-  if (requested == 0) return pa::kDefaultPartition;
-  if (requested < 16 || requested > pa::kMaxPartition || requested % 16 != 0) return -1;
-  return requested;
+// 0 = balanced form; otherwise a fixed partition size (multiple of 16).
+bool partition_ok(int32_t requested) {
+  return requested == 0 ||
+         (requested >= 16 && requested <= pa::kMaxPartition && requested % 16 == 0);
 }
 
 int32_t num_partitions(int32_t max_context_len, int32_t partition) {
@@ -66,11 +72,49 @@ int32_t num_partitions(int32_t max_context_len, int32_t partition) {
   return np < 1 ? 1 : np;
 }
 
-size_t workspace_bytes_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                           int32_t max_partitions) {
-  if (max_partitions <= 1) return 0;
-  const size_t rows = size_t(num_seqs) * size_t(num_q_heads) * size_t(max_partitions);
-  return rows * size_t(head_dim + 2) * sizeof(float);
+// The form a call takes: the balanced single launch, or fixed partitions of
+// `*partition` tokens (the default size when the balanced form cannot plan
+// this many sequences).
+bool use_balanced(int32_t num_seqs, int32_t requested, int32_t *partition) {
+  if (requested == 0 && num_seqs <= pa::kMaxPlanSeqs) {
+    *partition = 0;
+    return true;
+  }
+  *partition = requested == 0 ? pa::kDefaultPartition : requested;
+  return false;
+}
+
+// Workspace layout: [arrival counters, int32 per (sequence, KV head)] then the
+// partials of the form in use. The counters are only touched by the balanced
+// form, which leaves them zero.
+struct WsLayout {
+  size_t counters = 0;  // bytes
+  size_t slots = 0;     // partial rows of `width` floats
+  size_t width = 0;     // floats per partial row of acc
+  size_t stats = 0;     // floats of m (and of l)
+  size_t total = 0;
+};
+
+WsLayout workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t max_context_len, int32_t requested) {
+  WsLayout w;
+  int32_t partition = 0;
+  w.counters = round_up(size_t(num_seqs) * size_t(num_kv_heads) * sizeof(int32_t));
+  if (use_balanced(num_seqs, requested, &partition)) {
+    const size_t group = size_t(num_q_heads / num_kv_heads);
+    w.slots = size_t(num_seqs) * num_kv_heads + pa::kMaxFlatWorkgroups;
+    w.width = group * head_dim;
+    w.stats = w.slots * group;
+  } else {
+    const int32_t parts = num_partitions(max_context_len, partition);
+    if (parts > 1) {
+      w.slots = size_t(num_seqs) * num_q_heads * parts;
+      w.width = size_t(head_dim);
+      w.stats = w.slots;
+    }
+  }
+  w.total = w.counters + round_up((w.slots * w.width + 2 * w.stats) * sizeof(float));
+  return w;
 }
 
 int32_t sync_copy_to_host(void *dst, const void *src, size_t bytes, hipStream_t stream) {
@@ -82,6 +126,35 @@ int32_t sync_copy_to_host(void *dst, const void *src, size_t bytes, hipStream_t 
 }
 
 }  // namespace
+
+namespace pa {
+
+int flat_grid_size(const void *kernel, int threads, size_t dynamic_lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void *, size_t>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  const auto key = std::make_tuple(dev, kernel, dynamic_lds);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dynamic_lds) !=
+      hipSuccess)
+    return -1;
+  if (const char *e = std::getenv("PA_FLAT_WGS_PER_CU")) {  // tuning knob
+    const int v = std::atoi(e);
+    if (v > 0) per_cu = v;
+  }
+  int grid = cus * (per_cu > 0 ? per_cu : 1);
+  if (grid > kMaxFlatWorkgroups) grid = kMaxFlatWorkgroups;
+  cache[key] = grid;
+  return grid;
+}
+
+}  // namespace pa
 
 extern "C" {
 
@@ -139,40 +212,25 @@ int32_t pa_reshape_and_cache(const void *key, const void *value, void *k_cache, 
   return pa::launch_reshape_and_cache(p, s) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t max_context_len, int32_t requested,
-                                 int32_t dtype) {
-  if (check_decode_shapes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                          dtype) != PA_OK)
-    return -1;
-  return resolve_partition(requested);
-}
-
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_context_len,
                                 int32_t partition_size, int32_t dtype) {
   if (check_decode_shapes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                           dtype) != PA_OK)
     return size_t(-1);
-  const int32_t part = resolve_partition(partition_size);
-  if (part < 0) return size_t(-1);
-  return workspace_bytes_for(num_seqs, num_q_heads, head_dim,
-                             num_partitions(max_context_len, part));
+  if (!partition_ok(partition_size)) return size_t(-1);
+  return workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                          partition_size)
+      .total;
 }
 
-}  // extern "C"
-
-namespace {
-
-// Validation shared by pa_decode and pa_decode_partitions; fills `p`.
-int32_t prepare_decode(pa::DecodeParams &p, void *out, const void *q, const void *k_cache,
-                       const void *v_cache, const int32_t *block_tables,
-                       const int32_t *context_lens, float scale, int32_t num_seqs,
-                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
-                       int32_t max_context_len, int32_t partition_size, int32_t dtype,
-                       void *workspace, size_t workspace_bytes, hipStream_t s, bool *no_work) {
-  *no_work = false;
+int32_t pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                  const int32_t *block_tables, const int32_t *context_lens, float scale,
+                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                  int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size,
+                  int32_t dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int32_t st = check_decode_shapes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                    max_context_len, dtype);
   if (st != PA_OK) return st;
@@ -181,20 +239,20 @@ int32_t prepare_decode(pa::DecodeParams &p, void *out, const void *q, const void
   if (int64_t(max_context_len) > int64_t(max_blocks_per_seq) * block_size) return PA_ERR_BAD_SHAPE;
   if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
     return PA_ERR_BAD_SHAPE;
-  const int32_t part = resolve_partition(partition_size);
-  if (part < 0) return PA_ERR_BAD_SHAPE;
-  if (num_seqs == 0) {
-    *no_work = true;
-    return PA_OK;
-  }
+  if (!partition_ok(partition_size)) return PA_ERR_BAD_SHAPE;
+  int32_t part = 0;
+  const bool balanced = use_balanced(num_seqs, partition_size, &part);
+  if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return PA_ERR_NULL_POINTER;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
-  const int32_t max_parts = num_partitions(max_context_len, part);
-  const size_t need = workspace_bytes_for(num_seqs, num_q_heads, head_dim, max_parts);
-  if (need > 0) {
+  const WsLayout lay = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                        max_context_len, partition_size);
+  const int32_t max_parts = balanced ? 1 : num_partitions(max_context_len, part);
+  const bool needs_ws = balanced || max_parts > 1;
+  if (needs_ws) {
     if (!workspace) return PA_ERR_NULL_POINTER;
-    if (workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
+    if (workspace_bytes < lay.total) return PA_ERR_WORKSPACE_TOO_SMALL;
     if (!aligned16(workspace)) return PA_ERR_UNSUPPORTED;
   }
 
@@ -214,16 +272,23 @@ int32_t prepare_decode(pa::DecodeParams &p, void *out, const void *q, const void
         if (b < 0 || b >= num_blocks) return PA_ERR_BAD_INDEX;
       }
     }
+    if (balanced) {  // the arrival counters must be zero
+      std::vector<int32_t> cnt(size_t(num_seqs) * num_kv_heads);
+      st = sync_copy_to_host(cnt.data(), workspace, sizeof(int32_t) * cnt.size(), s);
+      if (st != PA_OK) return st;
+      for (int32_t c : cnt)
+        if (c != 0) return PA_ERR_BAD_INDEX;
+    }
   }
 
-  p = pa::DecodeParams{};
+  pa::DecodeParams p{};
   p.out = out;
-  if (need > 0) {
-    const size_t rows = size_t(num_seqs) * num_q_heads * max_parts;
-    float *ws = static_cast<float *>(workspace);
-    p.ws_acc = ws;
-    p.ws_m = ws + rows * head_dim;
-    p.ws_l = p.ws_m + rows;
+  if (needs_ws) {
+    char *ws = static_cast<char *>(workspace);
+    p.ws_count = reinterpret_cast<int32_t *>(ws);
+    p.ws_acc = reinterpret_cast<float *>(ws + lay.counters);
+    p.ws_m = p.ws_acc + lay.slots * lay.width;
+    p.ws_l = p.ws_m + lay.stats;
   }
   p.q = q;
   p.k_cache = k_cache;
@@ -239,95 +304,11 @@ int32_t prepare_decode(pa::DecodeParams &p, void *out, const void *q, const void
   p.num_blocks = num_blocks;
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.max_context_len = max_context_len;
-  p.partition_size = part;
+  p.partition_size = balanced ? 0 : part;
   p.max_partitions = max_parts;
   p.dtype = dtype;
-  return PA_OK;
-}
-
-int32_t decode_stage(pa::DecodeStage stage, void *out, const void *q, const void *k_cache,
-                     const void *v_cache, const int32_t *block_tables,
-                     const int32_t *context_lens, float scale, int32_t num_seqs,
-                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                     int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
-                     int32_t max_context_len, int32_t partition_size, int32_t dtype,
-                     void *workspace, size_t workspace_bytes, void *stream) {
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  pa::DecodeParams p;
-  bool no_work = false;
-  const int32_t st = prepare_decode(p, out, q, k_cache, v_cache, block_tables, context_lens,
-                                    scale, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                    block_size, num_blocks, max_blocks_per_seq, max_context_len,
-                                    partition_size, dtype, workspace, workspace_bytes, s,
-                                    &no_work);
-  if (st != PA_OK || no_work) return st;
+  const pa::DecodeStage stage = balanced ? pa::kStageFlat : pa::kStageBoth;
   return pa::launch_decode(p, s, stage) == hipSuccess ? PA_OK : PA_ERR_HIP;
-}
-
-}  // namespace
-
-extern "C" {
-
-int32_t pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
-                  const int32_t *block_tables, const int32_t *context_lens, float scale,
-                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                  int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size,
-                  int32_t dtype, void *workspace, size_t workspace_bytes, void *stream) {
-  return decode_stage(pa::kStageBoth, out, q, k_cache, v_cache, block_tables, context_lens,
-                      scale, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                      num_blocks, max_blocks_per_seq, max_context_len, partition_size, dtype,
-                      workspace, workspace_bytes, stream);
-}
-
-int32_t pa_decode_partitions(void *out, const void *q, const void *k_cache, const void *v_cache,
-                             const int32_t *block_tables, const int32_t *context_lens,
-                             float scale, int32_t num_seqs, int32_t num_q_heads,
-                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                             int32_t num_blocks, int32_t max_blocks_per_seq,
-                             int32_t max_context_len, int32_t partition_size, int32_t dtype,
-                             void *workspace, size_t workspace_bytes, void *stream) {
-  return decode_stage(pa::kStagePartitions, out, q, k_cache, v_cache, block_tables,
-                      context_lens, scale, num_seqs, num_q_heads, num_kv_heads, head_dim,
-                      block_size, num_blocks, max_blocks_per_seq, max_context_len,
-                      partition_size, dtype, workspace, workspace_bytes, stream);
-}
-
-int32_t pa_decode_reduce(void *out, const int32_t *context_lens, int32_t num_seqs,
-                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                         int32_t max_context_len, int32_t partition_size, int32_t dtype,
-                         const void *workspace, size_t workspace_bytes, void *stream) {
-  int32_t st = check_decode_shapes(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                   max_context_len, dtype);
-  if (st != PA_OK) return st;
-  const int32_t part = resolve_partition(partition_size);
-  if (part < 0) return PA_ERR_BAD_SHAPE;
-  const int32_t max_parts = num_partitions(max_context_len, part);
-  const size_t need = workspace_bytes_for(num_seqs, num_q_heads, head_dim, max_parts);
-  if (num_seqs == 0 || need == 0) return PA_OK;
-  if (!out || !context_lens || !workspace) return PA_ERR_NULL_POINTER;
-  if (workspace_bytes < need) return PA_ERR_WORKSPACE_TOO_SMALL;
-  if (!aligned16(workspace)) return PA_ERR_UNSUPPORTED;
-  pa::DecodeParams p{};
-  const size_t rows = size_t(num_seqs) * num_q_heads * max_parts;
-  float *ws = static_cast<float *>(const_cast<void *>(workspace));
-  p.out = out;
-  p.ws_acc = ws;
-  p.ws_m = ws + rows * head_dim;
-  p.ws_l = p.ws_m + rows;
-  p.context_lens = context_lens;
-  p.num_seqs = num_seqs;
-  p.num_kv_heads = num_kv_heads;
-  p.group = num_q_heads / num_kv_heads;
-  p.head_dim = head_dim;
-  p.max_context_len = max_context_len;
-  p.partition_size = part;
-  p.max_partitions = max_parts;
-  p.dtype = dtype;
-  return pa::launch_decode(p, reinterpret_cast<hipStream_t>(stream), pa::kStageReduce) ==
-                 hipSuccess
-             ? PA_OK
-             : PA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -6,33 +6,49 @@
 // softmax-normalised, and used to average the cached values. The cached rows
 // are found through the sequence's block table (§3.3).
 //
-// How (one workgroup per (context partition, KV head, sequence); split-K and a
-// log-sum-exp combine in the manner of flash decoding, [INFRA] Q2 of §8):
+// How. Split-K in the manner of flash decoding ([INFRA] Q2 of §8): the
+// context of each (sequence, KV head) is cut into pieces, each piece is reduced
+// to (running max, sum of weights, weighted sum of values), and the pieces are
+// combined by a log-sum-exp reduction. Two ways of cutting:
+//   decode_flat_kernel       balanced form: the whole (sequence, KV head, tile)
+//                            space is divided evenly among the resident
+//                            workgroups, one launch, split heads combined by
+//                            the last workgroup to finish;
+//   decode_partition_kernel  fixed partitions of P tokens, one workgroup each,
+//                            then decode_reduce_kernel.
+// Four waves per workgroup. All G query heads of a KV head share every K/V
+// byte read ([INFRA] §2.1, GQA).
 //
-// * A partition is `partition_size` consecutive tokens of one sequence. Its
-//   four waves take rounds of 16*TR tokens in turn. The partition's table
-//   entries are staged in LDS once, so every lane finds its token's physical
-//   block with one LDS read.
-// * Keys: QK^T runs on the matrix cores. For each 16-token tile, MFMA operand B
-//   is K^T (column = token, lane l holds 16 contiguous bytes of token l%16),
-//   operand A is the group's queries (row = query head, replicated over the
-//   four row groups when the group has fewer than four heads). The 16x16
-//   result leaves each token's score for every head of the group in the lane
-//   that loaded that token, so no cross-lane sum is needed. All G query heads
-//   of a KV head share each K tile read ([INFRA] §2.1 GQA).
-// * Values: loaded as whole contiguous rows (16 bytes per lane, 64 lanes
-//   covering 1 KB), so each lane owns 16 bytes of dims of a few tokens. The
-//   softmax weight of each token is fetched from the lane holding its score
-//   (ds_bpermute) and accumulated in float32 on the vector ALUs.
-// * Softmax is online per round in the log2 domain: the wave keeps the running
-//   maximum per head (wave-uniform) and rescales its partial sums when it grows.
-// * Tokens past the partition's end or the context are never read from
-//   unused slots: their addresses are clamped to the last valid token and
-//   their scores set to -inf, so their weights are exactly 0 and poisoned
-//   (NaN) pad slots cannot leak into the output.
-// * The four waves merge through LDS. A sequence with one partition writes the
-//   output directly; otherwise (m, l, acc) of the partition go to the
-//   workspace and decode_reduce_kernel combines them.
+// * Work of a workgroup: a segment (a token range of one sequence and KV
+//   head) is cut into windows; each of the four waves takes a contiguous chunk
+//   of a window that touches at most 64 blocks. The wave loads the chunk's
+//   table entries once, one per lane (clamped into the pool), so a 16-token
+//   tile's physical block is a v_readlane away and tile base addresses live in
+//   scalar registers.
+// * Rounds: a wave takes NT 16-token tiles per round. The next round's K and V
+//   loads are issued before the current round is consumed (two register
+//   buffers, with a scheduling barrier so the compiler cannot sink the loads to
+//   their uses; the loop holds no other memory operation), which keeps 16-32
+//   KB per wave in flight: the path is bound by HBM reads, not arithmetic.
+// * QK^T on the matrix cores (v_mfma 16x16x32 f16/bf16, 16x16x4 f32). Operand
+//   A is the K tile (row m = a token, loaded as 16 rows x 64 bytes per load),
+//   operand B the group's queries (column n = query head n % G). The tile's
+//   tokens are assigned to A rows through a fixed permutation chosen so that
+//   result slot i of lane l is the score of exactly the token whose V row
+//   segment lane l loads in V load i: scores never cross lanes for MHA.
+// * V is loaded as whole contiguous rows (64 lanes x 16 bytes = 1 KB per load;
+//   a "token group" of 8 or 16 lanes holds one token's row) and accumulated in
+//   float32 on the vector ALUs. With G > 1 a lane computes the softmax weight
+//   of its own head (n % G) and the other heads' weights arrive by DPP/swizzle
+//   from the lanes of the same token group.
+// * Online softmax in the log2 domain, per (token group, head): each token
+//   group keeps its own running maximum, so the loop has no cross-lane max.
+// * Masking by select: scores of tokens at or past the context end are -inf and
+//   their V values are replaced by 0, so NaN in unused slots cannot leak. Table
+//   entries are clamped into [0, num_blocks), so no load leaves the pool.
+// * Epilogue: token groups merge across lanes (shuffles), waves through LDS. A
+//   piece that is a whole (sequence, KV head) writes its output rows;
+//   otherwise its (max, sum, weighted values) go to the workspace.
 #include "pa_common.h"
 #include "pa_internal.h"
 
@@ -40,23 +56,22 @@ namespace pa {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kTabCache = kMaxPartition / 8 + 8;  // table entries one partition spans
 
-template <int DT, int D, int G> struct DecodeShape {
+template <int DT, int D, int G, int NT> struct DecodeShape {
   static constexpr int E = Elem<DT>::kBytes;
-  static constexpr int EPC = Elem<DT>::kPerChunk;  // elements per 16-byte chunk
-  static constexpr int CPR = D * E / 16;           // chunks per token row
-  static constexpr int CPL = CPR / 4;              // K chunks per lane per tile
-  static constexpr int LPT = CPR;                  // V: lanes per token
-  static constexpr int TPI = kWave / LPT;          // V: tokens per load instruction
-  static constexpr int NVI = 16 / TPI;             // V: load instructions per tile
-  static constexpr int GH = G < 4 ? G : 4;         // query heads per MFMA head group
-  static constexpr int NHG = (G + 3) / 4;          // MFMA head groups
-  static constexpr int TR = CPL >= 8 ? 1 : 8 / CPL;  // tiles per round
-  static constexpr int ROUND = 16 * TR;            // tokens per round
-  static_assert(CPR >= 4 && CPR <= 64 && (CPR & (CPR - 1)) == 0, "row must be 4..64 chunks");
-  static_assert(NVI == CPL, "V instructions per tile equal K chunks per lane");
+  static constexpr int EPC = Elem<DT>::kPerChunk;    // elements per 16-byte chunk
+  static constexpr int ROWB = D * E;                 // bytes of one token's row
+  static constexpr int SEGB = ROWB < 256 ? ROWB : 256;  // row segment one token group loads
+  static constexpr int NSEG = ROWB / SEGB;           // segments per row (1 or 2)
+  static constexpr int LPT = SEGB / 16;              // lanes per token group (8 or 16)
+  static constexpr int TPI = kWave / LPT;            // tokens per V load (8 or 4)
+  static constexpr int VI = 16 / TPI;                // V loads per tile and segment
+  static constexpr int NV = VI * NSEG;               // V loads per tile
+  static constexpr int KS = ROWB / 64;               // K loads per tile (MFMA k-steps of 64 B)
+  static constexpr int ROUND = 16 * NT;              // tokens per round
+  static_assert(ROWB == 128 || ROWB == 256 || ROWB == 512, "row must be 128, 256 or 512 bytes");
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
+  static_assert(G <= LPT, "a token group must hold every head of the group");
 };
 
 // acc += A(16 x k) * B(k x 16) over one 16-byte chunk of the contraction.
@@ -79,22 +94,374 @@ template <> __device__ __forceinline__ f32x4 mfma_chunk<PA_F32>(const u32x4 &a, 
   return acc;
 }
 
-template <int DT, int D, int G>
+// Token (0..15, within a 16-token tile) that MFMA row m stands for. Result slot
+// j of lane l is row 4*(l/16) + j; the permutation makes that the token lane l
+// holds in V load j (LPT 16) or 2*(j/2)... (LPT 8), see the header comment.
+template <int LPT> __device__ __forceinline__ int tile_token_of_row(int m) {
+  const int g = m >> 2, j = m & 3;
+  if (LPT == 16) return 4 * j + g;
+  return 8 * (j >> 1) + 2 * g + (j & 1);
+}
+
+// Value of v in the lane of this lane's token group whose own head is h.
+template <int G> __device__ __forceinline__ float from_head(float v, int h) {
+  if (G == 1) return v;
+  const int iv = __builtin_bit_cast(int, v);
+  if (G <= 4) {
+    // quad_perm [h, h, h, h]: lane (l & ~3) | h
+    switch (h) {
+      case 0: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0x00, 0xF, 0xF, false));
+      case 1: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0x55, 0xF, 0xF, false));
+      case 2: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0xAA, 0xF, 0xF, false));
+      default: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0xFF, 0xF, 0xF, false));
+    }
+  }
+  // bitmask swizzle inside 32-lane halves: lane (l & 0x18) | h
+  switch (h) {
+    case 0: return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(iv, 0x18 | (0 << 5)));
+    case 1: return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(iv, 0x18 | (1 << 5)));
+    case 2: return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(iv, 0x18 | (2 << 5)));
+    case 3: return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(iv, 0x18 | (3 << 5)));
+    case 4: return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(iv, 0x18 | (4 << 5)));
+    case 5: return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(iv, 0x18 | (5 << 5)));
+    case 6: return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(iv, 0x18 | (6 << 5)));
+    default: return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(iv, 0x18 | (7 << 5)));
+  }
+}
+
+template <int DT, int D, int G, int NT> struct RoundBuf {
+  using S = DecodeShape<DT, D, G, NT>;
+  u32x4 k[NT][S::KS];
+  u32x4 v[NT][S::NV];
+};
+
+// Per-wave constants of the loop over one chunk of a segment (a token range
+// of one sequence and KV head). The chunk's table entries (at most 64) are
+// held one per lane: lane i has the entry of block first_blk + i.
+struct WaveCtx {
+  const char *k_cache;
+  const char *v_cache;
+  int64_t head_off;   // kv head offset inside a block, bytes
+  int64_t blk_bytes;  // bytes of one physical block (all kv heads)
+  int tabv;           // clamped table entry of block first_blk + lane
+  int first_blk;      // first block of the chunk
+  int bshift;
+  uint32_t koff;      // K lane offset in its tile (16-token blocks and larger)
+  uint32_t koff8;     // K lane offset in its block (8-token blocks)
+  uint32_t voff;      // V lane offset inside a V load
+  bool khi;           // 8-token blocks: this lane's K row is in the tile's second block
+};
+
+// 16-byte load at a wave-uniform base plus a per-lane 32-bit offset (the
+// global_load saddr form: the base stays in scalar registers).
+__device__ __forceinline__ u32x4 load_at(const char *base, uint32_t off) {
+  return *reinterpret_cast<const u32x4 *>(base + off);
+}
+
+// Issue the K and V loads of the round starting at token rtok (wave-uniform).
+template <bool BS8, int DT, int D, int G, int NT>
+__device__ __forceinline__ void load_round(RoundBuf<DT, D, G, NT> &R, const WaveCtx &c, int rtok) {
+  using S = DecodeShape<DT, D, G, NT>;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int tt = rtok + 16 * t;
+    const int local0 = min((tt >> c.bshift) - c.first_blk, 63);
+    const int phys0 = __builtin_amdgcn_readlane(c.tabv, local0);
+    if (!BS8) {
+      // The whole tile lies in one block: scalar base, per-lane constant offsets.
+      const int64_t base = (int64_t)phys0 * c.blk_bytes + c.head_off +
+                           (int64_t)(tt & ((1 << c.bshift) - 1)) * S::ROWB;
+      const char *kb = c.k_cache + base;
+      const char *vb = c.v_cache + base;
+#pragma unroll
+      for (int s = 0; s < S::KS; ++s) R.k[t][s] = load_at(kb, c.koff + s * 64);
+#pragma unroll
+      for (int i = 0; i < S::VI; ++i)
+#pragma unroll
+        for (int sg = 0; sg < S::NSEG; ++sg)
+          R.v[t][i * S::NSEG + sg] = load_at(vb, c.voff + i * S::TPI * S::ROWB + sg * S::SEGB);
+    } else {
+      // 8-token blocks: the tile spans two blocks.
+      const int phys1 = __builtin_amdgcn_readlane(c.tabv, min(local0 + 1, 63));
+      const int64_t base0 = (int64_t)phys0 * c.blk_bytes + c.head_off;
+      const int64_t base1 = (int64_t)phys1 * c.blk_bytes + c.head_off;
+      const char *kb = c.k_cache + (c.khi ? base1 : base0);
+#pragma unroll
+      for (int s = 0; s < S::KS; ++s) R.k[t][s] = load_at(kb, c.koff8 + s * 64);
+#pragma unroll
+      for (int i = 0; i < S::VI; ++i) {
+        const int first = i * S::TPI;  // tile token of this load's first row
+        const char *vb = c.v_cache + (first < 8 ? base0 : base1);
+#pragma unroll
+        for (int sg = 0; sg < S::NSEG; ++sg)
+          R.v[t][i * S::NSEG + sg] = load_at(vb, c.voff + (first & 7) * S::ROWB + sg * S::SEGB);
+      }
+    }
+  }
+}
+
+// Online-softmax state of one lane: its own head's running max and sum for its
+// token group, and the weighted V sums of every head for its row chunk(s).
+template <int DT, int D, int G, int NT> struct SoftState {
+  using S = DecodeShape<DT, D, G, NT>;
+  float m;
+  float l;
+  float acc[G][S::NSEG][S::EPC];
+};
+
+template <bool MASK, int DT, int D, int G, int NT>
+__device__ __forceinline__ void consume_round(const RoundBuf<DT, D, G, NT> &R,
+                                              SoftState<DT, D, G, NT> &st, const u32x4 *qb,
+                                              float scale_log2, int rtok, int p_end) {
+  using S = DecodeShape<DT, D, G, NT>;
+  const int lane = __lane_id();
+  const bool odd8 = (lane & 15) >= 8;          // LPT 8: second token group of the row
+  const int vtok = lane / S::LPT;              // token of this lane inside a V load
+
+  // Scores of this lane's own head for the tokens of its V loads.
+  float x[NT][S::VI];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < S::KS; ++s) a = mfma_chunk<DT>(R.k[t][s], qb[s], a);
+#pragma unroll
+    for (int i = 0; i < S::VI; ++i) {
+      float v;
+      if (S::LPT == 16) v = a[i];
+      else v = odd8 ? a[2 * i + 1] : a[2 * i];
+      v *= scale_log2;
+      if (MASK) {
+        const int tok = rtok + 16 * t + i * S::TPI + vtok;
+        v = tok < p_end ? v : -INFINITY;
+      }
+      x[t][i] = v;
+    }
+  }
+
+  float mx = x[0][0];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < S::VI; ++i) mx = fmaxf(mx, x[t][i]);
+  const float m_new = fmaxf(st.m, mx);
+  const float m_safe = m_new == -INFINITY ? 0.0f : m_new;
+  const float alpha = fast_exp2(st.m - m_safe);
+  st.m = m_new;
+  float psum = 0.0f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < S::VI; ++i) {
+      x[t][i] = fast_exp2(x[t][i] - m_safe);
+      psum += x[t][i];
+    }
+  st.l = fmaf(st.l, alpha, psum);
+
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float ah = from_head<G>(alpha, h);
+#pragma unroll
+    for (int sg = 0; sg < S::NSEG; ++sg)
+#pragma unroll
+      for (int e = 0; e < S::EPC; ++e) st.acc[h][sg][e] *= ah;
+  }
+
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int i = 0; i < S::VI; ++i) {
+      bool valid = true;
+      if (MASK) valid = rtok + 16 * t + i * S::TPI + vtok < p_end;
+      float vf[S::NSEG][S::EPC];
+#pragma unroll
+      for (int sg = 0; sg < S::NSEG; ++sg)
+#pragma unroll
+        for (int e = 0; e < S::EPC; ++e) {
+          const float f = chunk_elem<DT>(R.v[t][i * S::NSEG + sg], e);
+          vf[sg][e] = (MASK && !valid) ? 0.0f : f;
+        }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float ph = from_head<G>(x[t][i], h);
+#pragma unroll
+        for (int sg = 0; sg < S::NSEG; ++sg)
+#pragma unroll
+          for (int e = 0; e < S::EPC; ++e) st.acc[h][sg][e] = fmaf(ph, vf[sg][e], st.acc[h][sg][e]);
+      }
+    }
+  }
+}
+
+// WG-shared buffers of the epilogue (the waves' merged partial results).
+template <int G, int D> struct MergeLds {
+  float acc[kWaves][G][D];
+  float m[kWaves][G];
+  float l[kWaves][G];
+};
+
+// Tiles of a wave's chunk inside one window: at most 64 blocks of table.
+template <bool BS8> constexpr int chunk_tiles() { return BS8 ? 32 : 63; }
+
+// A segment [p_start, p_end) of sequence `seq`, KV head `kh`, processed by the
+// four waves. The segment is cut into windows of up to 4 * chunk_tiles tiles;
+// each wave takes a contiguous quarter of a window (a chunk that touches at
+// most 64 table entries), and runs its rounds of NT tiles through the
+// double-buffered loop. Leaves each wave's merged (max, sum, weighted values)
+// per head in LDS; the caller synchronises the workgroup before reading them.
+template <int DT, int D, int G, int NT, bool BS8>
+__device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int kh, int p_start,
+                                            int p_end, int wave, MergeLds<G, D> &lds) {
+  using S = DecodeShape<DT, D, G, NT>;
+  const int lane = __lane_id();
+  const int num_q_heads = p.num_kv_heads * G;
+  const int32_t *table_row = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
+
+  WaveCtx c;
+  c.k_cache = reinterpret_cast<const char *>(p.k_cache);
+  c.v_cache = reinterpret_cast<const char *>(p.v_cache);
+  c.bshift = p.block_shift;
+  c.blk_bytes = (int64_t)p.num_kv_heads * (S::ROWB << c.bshift);
+  c.head_off = (int64_t)kh * (S::ROWB << c.bshift);
+  {
+    const int ktok = tile_token_of_row<S::LPT>(lane & 15);
+    c.koff = ktok * S::ROWB + (lane >> 4) * 16;
+    c.koff8 = (ktok & 7) * S::ROWB + (lane >> 4) * 16;
+    c.khi = ktok >= 8;
+    c.voff = (lane / S::LPT) * S::ROWB + (lane % S::LPT) * 16;
+  }
+
+  // MFMA operand B: lane l holds query head (l % 16) % G, chunk (l / 16) + 4 s.
+  u32x4 qb[S::KS];
+  {
+    const int head = kh * G + ((lane & 15) % G);
+    const char *qrow = reinterpret_cast<const char *>(p.q) + ((int64_t)seq * num_q_heads + head) * S::ROWB;
+#pragma unroll
+    for (int s = 0; s < S::KS; ++s) qb[s] = load_chunk(qrow, ((lane >> 4) + 4 * s) * 16);
+  }
+
+  SoftState<DT, D, G, NT> st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int sg = 0; sg < S::NSEG; ++sg)
+#pragma unroll
+      for (int e = 0; e < S::EPC; ++e) st.acc[h][sg][e] = 0.0f;
+
+  const float sl2 = p.scale_log2;
+  const int seg_tiles = (p_end - p_start + 15) >> 4;
+  constexpr int kWin = kWaves * chunk_tiles<BS8>();
+  for (int w0 = 0; w0 < seg_tiles; w0 += kWin) {
+    const int win = min(kWin, seg_tiles - w0);
+    const int t0 = w0 + wave * win / kWaves;
+    const int t1 = w0 + (wave + 1) * win / kWaves;
+    if (t0 >= t1) continue;
+    const int tok0 = p_start + 16 * t0;
+    const int tok_end = min(p_start + 16 * t1, p_end);
+    c.first_blk = tok0 >> c.bshift;
+    {
+      const int idx = min(c.first_blk + lane, p.max_blocks_per_seq - 1);
+      c.tabv = min(max(table_row[idx], 0), p.num_blocks - 1);  // never address outside the pool
+    }
+    const int nr = (t1 - t0 + NT - 1) / NT;
+    auto rtok_of = [&](int r) { return tok0 + r * S::ROUND; };
+
+    // Two register buffers; at the top of the loop only A (round r) is in flight.
+    RoundBuf<DT, D, G, NT> A, B;
+    load_round<BS8>(A, c, rtok_of(0));
+    int r = 0;
+    while (r + 2 < nr) {
+      load_round<BS8>(B, c, rtok_of(r + 1));
+      __builtin_amdgcn_sched_barrier(0);
+      consume_round<false>(A, st, qb, sl2, rtok_of(r), tok_end);
+      load_round<BS8>(A, c, rtok_of(r + 2));
+      __builtin_amdgcn_sched_barrier(0);
+      consume_round<false>(B, st, qb, sl2, rtok_of(r + 1), tok_end);
+      r += 2;
+    }
+    // Rounds r and (if it exists) r + 1 remain; only the chunk's last round can be partial.
+    if (r + 1 < nr) {
+      load_round<BS8>(B, c, rtok_of(r + 1));
+      __builtin_amdgcn_sched_barrier(0);
+      consume_round<false>(A, st, qb, sl2, rtok_of(r), tok_end);
+      consume_round<true>(B, st, qb, sl2, rtok_of(r + 1), tok_end);
+    } else {
+      consume_round<true>(A, st, qb, sl2, rtok_of(r), tok_end);
+    }
+  }
+
+  // Merge the token groups of the wave (lanes l, l ^ LPT, l ^ 2 LPT, ... hold the
+  // same row chunk for different tokens).
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float mg = from_head<G>(st.m, h);
+    float mw = mg;
+#pragma unroll
+    for (int mask = S::LPT; mask < kWave; mask <<= 1) mw = fmaxf(mw, __shfl_xor(mw, mask));
+    const float f = mw == -INFINITY ? 0.0f : fast_exp2(mg - mw);
+    float lw = from_head<G>(st.l, h) * f;
+#pragma unroll
+    for (int mask = S::LPT; mask < kWave; mask <<= 1) lw += __shfl_xor(lw, mask);
+#pragma unroll
+    for (int sg = 0; sg < S::NSEG; ++sg)
+#pragma unroll
+      for (int e = 0; e < S::EPC; ++e) {
+        float a = st.acc[h][sg][e] * f;
+#pragma unroll
+        for (int mask = S::LPT; mask < kWave; mask <<= 1) a += __shfl_xor(a, mask);
+        st.acc[h][sg][e] = a;
+      }
+    if (lane < S::LPT) {
+#pragma unroll
+      for (int sg = 0; sg < S::NSEG; ++sg)
+#pragma unroll
+        for (int e = 0; e < S::EPC; ++e)
+          lds.acc[wave][h][sg * (S::SEGB / S::E) + lane * S::EPC + e] = st.acc[h][sg][e];
+    }
+    if (lane == 0) {
+      lds.m[wave][h] = mw;
+      lds.l[wave][h] = lw;
+    }
+  }
+}
+
+// The workgroup's combined (max, numerator, denominator) of element (h, d).
+template <int G, int D>
+__device__ __forceinline__ void wg_combine(const MergeLds<G, D> &lds, int h, int d, float &mmax,
+                                           float &num, float &den) {
+  mmax = lds.m[0][h];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) mmax = fmaxf(mmax, lds.m[w][h]);
+  num = 0.0f;
+  den = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float f = lds.m[w][h] == -INFINITY ? 0.0f : fast_exp2(lds.m[w][h] - mmax);
+    num = fmaf(f, lds.acc[w][h][d], num);
+    den = fmaf(f, lds.l[w][h], den);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fixed partitions: one workgroup per (partition, KV head, sequence).
+// ---------------------------------------------------------------------------
+
+template <int DT, int D, int G, int NT, bool BS8>
 __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams p) {
-  using S = DecodeShape<DT, D, G>;
   using OutT = typename Store<DT>::T;
-  constexpr int E = S::E;
+  __shared__ MergeLds<G, D> lds;
 
   const int part = blockIdx.x;
   const int kh = blockIdx.y;
   const int seq = blockIdx.z;
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int num_q_heads = p.num_kv_heads * G;
-  const int n = min(p.context_lens[seq], p.max_context_len);
   const int p_start = part * p.partition_size;
   OutT *out = reinterpret_cast<OutT *>(p.out);
+  const int n = min(p.context_lens[seq], p.max_context_len);
 
   if (n <= 0) {  // empty context: zero output rows
     if (part == 0)
@@ -104,163 +471,15 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   }
   if (p_start >= n) return;
   const int p_end = min(p_start + p.partition_size, n);
-  const int bshift = p.block_shift;
-  const int bmask = (1 << bshift) - 1;
-
-  // Table entries of this partition -> LDS.
-  __shared__ int s_tab[kTabCache];
-  const int first_blk = p_start >> bshift;
-  const int nblk = ((p_end - 1) >> bshift) - first_blk + 1;
-  const int32_t *tab = p.block_tables + (int64_t)seq * p.max_blocks_per_seq + first_blk;
-  for (int i = tid; i < nblk; i += kThreads) {
-    const int b = tab[i];
-    s_tab[i] = min(max(b, 0), p.num_blocks - 1);  // never address outside the pool
-  }
-
-  // MFMA operand A: queries of the group, one 16-byte chunk per k-step.
-  const int r = lane & 15;  // token column of this lane in K tiles
-  const int c = lane >> 4;  // row group (selects the K chunk)
-  u32x4 qop[S::NHG][S::CPL];
-#pragma unroll
-  for (int hg = 0; hg < S::NHG; ++hg) {
-    const int head = hg * 4 + ((lane & 3) % S::GH);
-    const int64_t qbase = ((int64_t)seq * num_q_heads + kh * G + head) * D * E;
-#pragma unroll
-    for (int s = 0; s < S::CPL; ++s) qop[hg][s] = load_chunk(p.q, qbase + (c + 4 * s) * 16);
-  }
-
-  float m_run[G], l_run[G], acc[G][S::EPC];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m_run[h] = -INFINITY;
-    l_run[h] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < S::EPC; ++e) acc[h][e] = 0.0f;
-  }
-
-  const int64_t head_stride = (int64_t)1 << bshift;  // rows per (block, head)
-  const int vtok = lane / S::LPT;                     // V: token within an instruction
-  const int vchunk = lane % S::LPT;                   // V: chunk within the row
-  __syncthreads();
-
-  for (int rs = p_start + wave * S::ROUND; rs < p_end; rs += kWaves * S::ROUND) {
-    u32x4 kb[S::TR][S::CPL];
-    u32x4 vb[S::TR][S::NVI];
-#pragma unroll
-    for (int j = 0; j < S::TR; ++j) {
-      const int tb = rs + 16 * j;
-      const int tk = min(tb + r, p_end - 1);
-      const int64_t krow =
-          ((int64_t)s_tab[(tk >> bshift) - first_blk] * p.num_kv_heads + kh) * head_stride + (tk & bmask);
-#pragma unroll
-      for (int s = 0; s < S::CPL; ++s) kb[j][s] = load_chunk(p.k_cache, krow * (D * E) + (c + 4 * s) * 16);
-#pragma unroll
-      for (int i = 0; i < S::NVI; ++i) {
-        const int tv = min(tb + i * S::TPI + vtok, p_end - 1);
-        const int64_t vrow =
-            ((int64_t)s_tab[(tv >> bshift) - first_blk] * p.num_kv_heads + kh) * head_stride + (tv & bmask);
-        vb[j][i] = load_chunk(p.v_cache, vrow * (D * E) + vchunk * 16);
-      }
-    }
-
-    // Scores (log2 domain), masked past the partition end.
-    float x[S::TR][G];
-#pragma unroll
-    for (int j = 0; j < S::TR; ++j) {
-      const bool valid = rs + 16 * j + r < p_end;
-#pragma unroll
-      for (int hg = 0; hg < S::NHG; ++hg) {
-        f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < S::CPL; ++s) a = mfma_chunk<DT>(qop[hg][s], kb[j][s], a);
-#pragma unroll
-        for (int i = 0; i < S::GH; ++i) {
-          const int h = hg * 4 + i;
-          if (h < G) x[j][h] = valid ? a[i] * p.scale_log2 : -INFINITY;
-        }
-      }
-    }
-
-    // Online softmax update per head.
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mx = x[0][h];
-#pragma unroll
-      for (int j = 1; j < S::TR; ++j) mx = fmaxf(mx, x[j][h]);
-      mx = uniform_f32(row16_max(mx));
-      const float m_new = fmaxf(m_run[h], mx);
-      const float alpha = fast_exp2(m_run[h] - m_new);
-      m_run[h] = m_new;
-      l_run[h] *= alpha;
-#pragma unroll
-      for (int e = 0; e < S::EPC; ++e) acc[h][e] *= alpha;
-#pragma unroll
-      for (int j = 0; j < S::TR; ++j) x[j][h] = fast_exp2(x[j][h] - m_new);
-    }
-
-    // P V on the vector ALUs, float32 accumulation.
-#pragma unroll
-    for (int j = 0; j < S::TR; ++j) {
-#pragma unroll
-      for (int i = 0; i < S::NVI; ++i) {
-        const int src = i * S::TPI + vtok;  // lane (row group 0) holding this token's scores
-        float vf[S::EPC];
-#pragma unroll
-        for (int e = 0; e < S::EPC; ++e) vf[e] = chunk_elem<DT>(vb[j][i], e);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float pv = lane_read(x[j][h], src);
-          l_run[h] += pv;
-#pragma unroll
-          for (int e = 0; e < S::EPC; ++e) acc[h][e] = fmaf(pv, vf[e], acc[h][e]);
-        }
-      }
-    }
-  }
-
-  // Sum over the lanes that hold the same dims (different tokens).
-#pragma unroll
-  for (int mask = S::LPT; mask < kWave; mask <<= 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      l_run[h] += lane_xor(l_run[h], mask);
-#pragma unroll
-      for (int e = 0; e < S::EPC; ++e) acc[h][e] += lane_xor(acc[h][e], mask);
-    }
-  }
-
-  __shared__ float s_acc[kWaves][G][D];
-  __shared__ float s_m[kWaves][G];
-  __shared__ float s_l[kWaves][G];
-  if (lane < S::LPT) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < S::EPC; ++e) s_acc[wave][h][lane * S::EPC + e] = acc[h][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      s_m[wave][h] = m_run[h];
-      s_l[wave][h] = l_run[h];
-    }
-  }
+  run_segment<DT, D, G, NT, BS8>(p, seq, kh, p_start, p_end, wave, lds);
   __syncthreads();
 
   const bool single = n <= p.partition_size;
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int h = idx / D;
     const int d = idx % D;
-    float mmax = s_m[0][h];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) mmax = fmaxf(mmax, s_m[w][h]);
-    float num = 0.0f, den = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2(s_m[w][h] - mmax);
-      num = fmaf(f, s_acc[w][h][d], num);
-      den = fmaf(f, s_l[w][h], den);
-    }
+    float mmax, num, den;
+    wg_combine(lds, h, d, mmax, num, den);
     const int64_t row = (int64_t)seq * num_q_heads + kh * G + h;
     if (single) {
       out[row * D + d] = Store<DT>::cvt(num / den);
@@ -299,11 +518,225 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeParams p) {
   reinterpret_cast<OutT *>(p.out)[((int64_t)seq * num_q_heads + hq) * D + d] = Store<DT>::cvt(num / den);
 }
 
+// ---------------------------------------------------------------------------
+// Balanced schedule: the (sequence, KV head, 16-token tile) space, flattened in
+// that order, is cut into gridDim.x equal ranges, one per workgroup. A
+// workgroup walks its range as segments (the part of one (sequence, KV head)
+// inside the range). A segment that is a whole (sequence, KV head) writes its
+// output rows; the pieces of a split one leave partials in the workspace and
+// the last workgroup to finish a piece combines them (log-sum-exp), so one
+// launch does the whole decode and every workgroup moves the same number of
+// tiles whatever the mix of context lengths.
+// ---------------------------------------------------------------------------
+
+// Partials shared between workgroups are written and read at agent scope:
+// written through to the device-coherent level and read from it, never from a
+// stale per-XCD L2 line.
+__device__ __forceinline__ void publish(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float fetch(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup holding flattened tile x (ranges [floor(w T / N), floor((w+1) T / N)),
+// all non-empty since N <= T).
+__device__ __forceinline__ int wg_of_tile(int64_t x, int64_t total, int nwg) {
+  return (int)(((x + 1) * nwg - 1) / total);
+}
+
+template <int DT, int D, int G, int NT, bool BS8>
+__global__ __launch_bounds__(kThreads) void decode_flat_kernel(DecodeParams p) {
+  using OutT = typename Store<DT>::T;
+  extern __shared__ int s_plan[];  // tiles prefix [S + 1], clamped lengths [S]
+  __shared__ MergeLds<G, D> lds;
+  __shared__ int s_wsum[kWaves];
+  __shared__ int s_found;
+  __shared__ int s_last;
+
+  const int S = p.num_seqs;
+  const int hkv = p.num_kv_heads;
+  const int num_q_heads = hkv * G;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = blockIdx.x;
+  int *s_tc = s_plan;
+  int *s_n = s_plan + S + 1;
+  OutT *out = reinterpret_cast<OutT *>(p.out);
+
+  // Plan: tiles per sequence and their prefix sums (every workgroup computes the
+  // same plan from context_lens).
+  if (tid == 0) s_tc[0] = 0;
+  int carry = 0;
+  for (int base = 0; base < S; base += kThreads) {
+    const int s = base + tid;
+    int n = s < S ? min(p.context_lens[s], p.max_context_len) : 0;
+    n = max(n, 0);
+    int x = (n + 15) >> 4;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == kWave - 1) s_wsum[wave] = x;
+    __syncthreads();
+    int off = carry, total = 0;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      off += v < wave ? s_wsum[v] : 0;
+      total += s_wsum[v];
+    }
+    if (s < S) {
+      s_tc[s + 1] = off + x;
+      s_n[s] = n;
+    }
+    carry += total;
+    __syncthreads();
+  }
+  const int64_t total = (int64_t)hkv * carry;
+
+  // Empty contexts: zero output rows, spread over the workgroups.
+  for (int s = w; s < S; s += gridDim.x)
+    if (s_n[s] == 0)
+      for (int i = tid; i < num_q_heads * D; i += kThreads)
+        out[(int64_t)s * num_q_heads * D + i] = Store<DT>::cvt(0.0f);
+
+  // With fewer tiles than workgroups only the first `total` take part, so every
+  // range below is non-empty (the combine counts on that).
+  const int nwg = (int)min((int64_t)gridDim.x, total);
+  if (w >= nwg) return;
+  const int64_t start = (int64_t)w * total / nwg;
+  const int64_t end = (int64_t)(w + 1) * total / nwg;
+
+  // The sequence holding flattened tile `start`.
+  for (int s = tid; s < S; s += kThreads)
+    if ((int64_t)hkv * s_tc[s] <= start && start < (int64_t)hkv * s_tc[s + 1]) s_found = s;
+  __syncthreads();
+  int seq = __builtin_amdgcn_readfirstlane(s_found);
+
+  int64_t pos = start;
+  while (pos < end) {
+    while (pos >= (int64_t)hkv * s_tc[seq + 1]) ++seq;  // skips empty sequences
+    const int tiles = s_tc[seq + 1] - s_tc[seq];
+    const int64_t seq_base = (int64_t)hkv * s_tc[seq];
+    const int kh = (int)((pos - seq_base) / tiles);
+    const int64_t item_base = seq_base + (int64_t)kh * tiles;
+    const int a = (int)(pos - item_base);
+    const int b = (int)min(end - item_base, (int64_t)tiles);
+    const int n = s_n[seq];
+    const int p_start = 16 * a;
+    const int p_end = min(16 * b, n);
+
+    run_segment<DT, D, G, NT, BS8>(p, seq, kh, p_start, p_end, wave, lds);
+    __syncthreads();
+
+    const bool whole = a == 0 && b == tiles;
+    const int item = seq * hkv + kh;
+    const int first_wg = wg_of_tile(item_base, total, nwg);
+    const int64_t slot = (int64_t)item + w;  // distinct for every (item, workgroup) pair
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      const int h = idx / D;
+      const int d = idx % D;
+      float mmax, num, den;
+      wg_combine(lds, h, d, mmax, num, den);
+      if (whole) {
+        out[((int64_t)item * G + h) * D + d] = Store<DT>::cvt(num / den);
+      } else {
+        publish(p.ws_acc + (slot * G + h) * D + d, num);
+        if (d == 0) {
+          publish(p.ws_m + slot * G + h, mmax);
+          publish(p.ws_l + slot * G + h, den);
+        }
+      }
+    }
+    if (!whole) {
+      // Count this piece in; the item's last workgroup to arrive combines. The
+      // partials were written through to the device-coherent level (agent
+      // scope) and every thread waits for its writes to complete before the
+      // arrival is counted, so the last arriver, reading them back at agent
+      // scope, sees all of them. No L2 write-back or invalidate is needed.
+      const int last_wg = wg_of_tile(item_base + tiles - 1, total, nwg);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0)
+        s_last = __hip_atomic_fetch_add(p.ws_count + item, 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == last_wg - first_wg;
+      __syncthreads();
+      if (s_last) {
+        for (int idx = tid; idx < G * D; idx += kThreads) {
+          const int h = idx / D;
+          const int d = idx % D;
+          // One pass over the contributors with a running maximum, eight at a
+          // time so that their loads are in flight together.
+          float mrun = -INFINITY, num = 0.0f, den = 0.0f;
+          for (int j0 = first_wg; j0 <= last_wg; j0 += 8) {
+            float mj[8], lj[8], aj[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const int64_t sl = (int64_t)item + min(j0 + u, last_wg);
+              mj[u] = fetch(p.ws_m + sl * G + h);
+              lj[u] = fetch(p.ws_l + sl * G + h);
+              aj[u] = fetch(p.ws_acc + (sl * G + h) * D + d);
+            }
+            float mnew = mrun;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              if (j0 + u <= last_wg) mnew = fmaxf(mnew, mj[u]);
+            const float sc = mrun == -INFINITY ? 0.0f : fast_exp2(mrun - mnew);
+            num *= sc;
+            den *= sc;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              if (j0 + u > last_wg) continue;
+              const float f = fast_exp2(mj[u] - mnew);
+              num = fmaf(f, aj[u], num);
+              den = fmaf(f, lj[u], den);
+            }
+            mrun = mnew;
+          }
+          out[((int64_t)item * G + h) * D + d] = Store<DT>::cvt(num / den);
+        }
+        if (tid == 0)  // leave the counter zero for the next call
+          __hip_atomic_store(p.ws_count + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();  // lds and s_last are reused by the next segment
+    pos = item_base + b;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launch
+// ---------------------------------------------------------------------------
+
+template <int DT, int D, int G> constexpr int rounds_tiles() {
+  return (D * Elem<DT>::kBytes) >= 256 ? 1 : 2;
+}
+
+template <int DT, int D, int G, bool BS8>
+static hipError_t launch_flat(const DecodeParams &p, hipStream_t stream) {
+  constexpr int NT = rounds_tiles<DT, D, G>();
+  auto kern = decode_flat_kernel<DT, D, G, NT, BS8>;
+  const size_t shmem = flat_plan_lds_bytes(p.num_seqs);
+  const int grid = flat_grid_size(reinterpret_cast<const void *>(kern), kThreads, shmem);
+  if (grid <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), shmem, stream, p);
+  return hipGetLastError();
+}
+
 template <int DT, int D, int G>
 static hipError_t launch_dtg(const DecodeParams &p, hipStream_t stream, DecodeStage stage) {
+  constexpr int NT = rounds_tiles<DT, D, G>();
+  const bool bs8 = p.block_shift == 3;
+  if (stage == kStageFlat)
+    return bs8 ? launch_flat<DT, D, G, true>(p, stream) : launch_flat<DT, D, G, false>(p, stream);
   if (stage != kStageReduce) {
     dim3 grid(p.max_partitions, p.num_kv_heads, p.num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<DT, D, G>), grid, dim3(kThreads), 0, stream, p);
+    if (bs8)
+      hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, NT, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, NT, false>), grid, dim3(kThreads), 0, stream, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -331,7 +764,9 @@ static hipError_t launch_d(const DecodeParams &p, hipStream_t stream, DecodeStag
   switch (p.head_dim) {
     case 64: return launch_dt<DT, 64>(p, stream, stage);
     case 128: return launch_dt<DT, 128>(p, stream, stage);
-    case 256: return launch_dt<DT, 256>(p, stream, stage);
+    case 256:
+      if constexpr (DT != PA_F32) return launch_dt<DT, 256>(p, stream, stage);
+      break;
   }
   return hipErrorInvalidValue;
 }

@@ -2,20 +2,27 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace pa {
 
-// Largest partition (tokens) a decode workgroup handles; bounds its LDS copy
-// of the block-table entries.
-constexpr int kMaxPartition = 2048;
+// Largest partition (tokens) a decode workgroup of the fixed-partition form
+// handles, and the default size of that form.
+constexpr int kMaxPartition = 4096;
 constexpr int kDefaultPartition = 256;
+
+// Balanced (single-launch) form: at most this many sequences (its plan of
+// per-sequence tile counts lives in LDS) and this many workgroups.
+constexpr int kMaxPlanSeqs = 4096;
+constexpr int kMaxFlatWorkgroups = 2048;
 
 struct DecodeParams {
   void *out;
-  float *ws_acc;  // [S, Hq, max_partitions, D] float32 partial numerators
-  float *ws_m;    // [S, Hq, max_partitions] running max (log2 domain)
-  float *ws_l;    // [S, Hq, max_partitions] partial denominators
+  float *ws_acc;      // partial numerators (layout depends on the form)
+  float *ws_m;        // partial maxima (log2 domain)
+  float *ws_l;        // partial denominators
+  int32_t *ws_count;  // balanced form: arrivals per (sequence, KV head); zero between calls
   const void *q;
   const void *k_cache;
   const void *v_cache;
@@ -48,9 +55,18 @@ struct CacheParams {
   int64_t num_slots;  // num_blocks * block_size
 };
 
-enum DecodeStage { kStageBoth = 0, kStagePartitions = 1, kStageReduce = 2 };
+// kStageFlat: balanced single launch. kStageBoth: fixed partitions, then the
+// reduce. kStagePartitions / kStageReduce: one of those two launches.
+enum DecodeStage { kStageBoth = 0, kStagePartitions = 1, kStageReduce = 2, kStageFlat = 3 };
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream, DecodeStage stage);
 hipError_t launch_reshape_and_cache(const CacheParams &p, hipStream_t stream);
+
+// Dynamic LDS of the balanced form's plan.
+inline size_t flat_plan_lds_bytes(int num_seqs) { return size_t(2 * num_seqs + 1) * sizeof(int); }
+
+// Workgroups of a balanced launch on the current device: as many as can be
+// resident at once (capped at kMaxFlatWorkgroups). Defined in pa_api.cpp.
+int flat_grid_size(const void *kernel, int threads, size_t dynamic_lds);
 
 }  // namespace pa

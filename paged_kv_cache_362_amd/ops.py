@@ -76,20 +76,22 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Ten
     _check("pa_reshape_and_cache", code)
 
 
-def partition_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                   max_context_len: int, dtype: torch.dtype, requested: int = 0) -> int:
-    p = lib().pa_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                       max_context_len, requested, dtype_code(dtype))
-    _require(p > 0, "invalid partition request")
-    return p
-
-
 def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                    max_context_len: int, dtype: torch.dtype, partition: int = 0) -> int:
+    """Bytes of decode scratch; ``partition`` 0 = balanced form, else fixed partitions."""
     size = lib().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                           max_context_len, partition, dtype_code(dtype))
     _require(size != ctypes.c_size_t(-1).value, "invalid workspace request")
     return size
+
+
+def new_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                  max_context_len: int, dtype: torch.dtype, device, partition: int = 0
+                  ) -> torch.Tensor:
+    """A zero-filled workspace (the library keeps its counters zero afterwards)."""
+    size = workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                          dtype, partition)
+    return torch.zeros(max(size, 16), dtype=torch.uint8, device=device)
 
 
 def _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, out,
@@ -110,9 +112,8 @@ def _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_le
     else:
         _on_gpu(out)
         _require(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
-    need = workspace_size(s, hq, hkv, d, max_context_len, q.dtype, partition)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = new_workspace(s, hq, hkv, d, max_context_len, q.dtype, q.device, partition)
     else:
         _on_gpu(workspace)
     return out, workspace
@@ -137,33 +138,13 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     """Paged decode attention; returns out [S, Hq, D] in q's dtype.
 
     ``max_context_len`` is the host-side maximum of ``context_lens``.
-    ``workspace`` (uint8, at least ``workspace_size(...)`` bytes) is allocated
-    here when not given.
+    ``partition`` 0 is the balanced single-launch form; a positive multiple of
+    16 selects fixed partitions of that many tokens. ``workspace`` (uint8, at
+    least ``workspace_size(...)`` bytes, zero-filled before its first use) is
+    allocated here when not given.
     """
     out, workspace = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
                                   max_context_len, out, workspace, partition)
     _launch_decode("pa_decode", q, k_cache, v_cache, block_tables, context_lens, scale,
                    max_context_len, out, workspace, partition)
     return out
-
-
-def decode_partitions(q, k_cache, v_cache, block_tables, context_lens, scale,
-                      max_context_len, out, workspace, partition: int = 0) -> None:
-    """First launch of ``decode`` (partition kernel); ``out``/``workspace`` are required."""
-    _require(out is not None and workspace is not None, "out and workspace are required")
-    _decode_args(q, k_cache, v_cache, block_tables, context_lens, max_context_len, out,
-                 workspace, partition)
-    _launch_decode("pa_decode_partitions", q, k_cache, v_cache, block_tables, context_lens,
-                   scale, max_context_len, out, workspace, partition)
-
-
-def decode_reduce(out, context_lens, num_kv_heads: int, max_context_len: int, workspace,
-                  partition: int = 0) -> None:
-    """Second launch of ``decode``: combine the partitions left in ``workspace``."""
-    _on_gpu(out, context_lens, workspace)
-    s, hq, d = out.shape
-    code = lib().pa_decode_reduce(
-        _dev_ptr(out), _dev_ptr(context_lens), s, hq, num_kv_heads, d, int(max_context_len),
-        int(partition), dtype_code(out.dtype), _dev_ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(out))
-    _check("pa_decode_reduce", code)

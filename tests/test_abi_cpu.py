@@ -32,8 +32,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("pa_reshape_and_cache", "pa_decode", "pa_decode_partitions", "pa_decode_reduce",
-              "pa_decode_workspace_size", "pa_decode_partition_size", "pa_status_str",
+    for n in ("pa_reshape_and_cache", "pa_decode", "pa_decode_workspace_size", "pa_status_str",
               "pa_abi_version"):
         assert n in names
 
@@ -45,29 +44,39 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.pa_abi_version() == 1
+    assert lib.pa_abi_version() == 2
     for code in range(7):
         assert lib.pa_status_str(code)
     assert lib.pa_status_str(99) == b"unknown status"
 
 
-def test_partition_policy(lib):
-    assert lib.pa_decode_partition_size(32, 32, 32, 128, 2048, 0, F16) == 256
-    assert lib.pa_decode_partition_size(32, 32, 32, 128, 2048, 64, F16) == 64
-    assert lib.pa_decode_partition_size(32, 32, 32, 128, 2048, 24, F16) == -1
-    assert lib.pa_decode_partition_size(32, 32, 32, 128, 2048, 4096, F16) == -1
-    assert lib.pa_decode_partition_size(32, 32, 32, 96, 2048, 0, F16) == -1
+def _counters(s, hkv):
+    return -(-s * hkv * 4 // 256) * 256
+
+
+def _floats(n):
+    return -(-n * 4 // 256) * 256
 
 
 def test_workspace_size(lib):
-    # one partition: nothing needed
-    assert lib.pa_decode_workspace_size(4, 8, 8, 128, 256, 256, F16) == 0
-    # S * Hq * partitions * (D + 2) * 4
-    assert lib.pa_decode_workspace_size(32, 32, 32, 128, 2048, 256, F16) == 32 * 32 * 8 * 130 * 4
-    assert lib.pa_decode_workspace_size(1, 32, 32, 64, 8192, 0, F16) == 32 * 32 * 66 * 4
+    # balanced form: counters, then (S * Hkv + 2048) slots of G * (D + 2) floats
+    assert lib.pa_decode_workspace_size(32, 32, 32, 128, 2048, 0, F16) == \
+        _counters(32, 32) + _floats((32 * 32 + 2048) * 130)
+    assert lib.pa_decode_workspace_size(64, 32, 8, 128, 4096, 0, BF16) == \
+        _counters(64, 8) + _floats((64 * 8 + 2048) * 4 * 130)
+    # fixed partitions: counters, then S * Hq * partitions * (D + 2) floats
+    assert lib.pa_decode_workspace_size(4, 8, 8, 128, 256, 256, F16) == _counters(4, 8)
+    assert lib.pa_decode_workspace_size(32, 32, 32, 128, 2048, 256, F16) == \
+        _counters(32, 32) + _floats(32 * 32 * 8 * 130)
+    # more sequences than the balanced form plans: fixed partitions of 256
+    assert lib.pa_decode_workspace_size(5000, 8, 8, 64, 1000, 0, F16) == \
+        _counters(5000, 8) + _floats(5000 * 8 * 4 * 66)
+    assert lib.pa_decode_workspace_size(1, 4, 4, 64, 100, 24, F16) == BAD_SIZE  # not x16
+    assert lib.pa_decode_workspace_size(1, 4, 4, 64, 100, 8192, F16) == BAD_SIZE  # > 4096
     assert lib.pa_decode_workspace_size(1, 6, 4, 64, 100, 0, F16) == BAD_SIZE  # 6 % 4
     assert lib.pa_decode_workspace_size(1, 12, 4, 64, 100, 0, F16) == BAD_SIZE  # group 3
     assert lib.pa_decode_workspace_size(1, 4, 4, 64, 100, 0, 7) == BAD_SIZE  # dtype
+    assert lib.pa_decode_workspace_size(1, 4, 4, 256, 100, 0, F32) == BAD_SIZE  # f32 D256
 
 
 def _decode(lib, **kw):
@@ -86,6 +95,7 @@ def test_decode_rejects_bad_arguments_before_launch(lib):
     assert _decode(lib, Hq=6) == SHAPE
     assert _decode(lib, Hq=12) == UNSUP
     assert _decode(lib, D=96) == UNSUP
+    assert _decode(lib, D=256) == UNSUP  # f32 rows of 1 KB are not built
     assert _decode(lib, B=12) == UNSUP
     assert _decode(lib, dtype=5) == UNSUP
     assert _decode(lib, maxlen=65) == SHAPE  # > M * B
@@ -93,8 +103,11 @@ def test_decode_rejects_bad_arguments_before_launch(lib):
     assert _decode(lib, part=20) == SHAPE
     assert _decode(lib, scale=float("nan")) == SHAPE
     assert _decode(lib, q=24) == UNSUP  # misaligned
-    assert _decode(lib, maxlen=50, part=16) == NULLP  # needs a workspace
+    assert _decode(lib, maxlen=50, part=16) == NULLP  # fixed form with two partitions
     assert _decode(lib, maxlen=50, part=16, ws=16, wsb=10) == WS
+    assert _decode(lib, maxlen=50) == NULLP  # the balanced form always needs one
+    assert _decode(lib, maxlen=50, ws=16, wsb=1000) == WS
+    assert _decode(lib, maxlen=50, ws=24, wsb=1 << 20) == UNSUP  # misaligned workspace
     assert _decode(lib, S=0, q=None, out=None) == OK  # empty batch: no work, no launch
 
 
@@ -107,23 +120,3 @@ def test_cache_write_rejects_bad_arguments_before_launch(lib):
     assert f(16, 16, 16, 16, 16, 1, 4, 64, 24, 8, F16, None) == UNSUP
     assert f(16, 16, 24, 16, 16, 1, 4, 64, 16, 8, F16, None) == UNSUP
     assert f(None, None, None, None, None, 0, 4, 64, 16, 8, F16, None) == OK
-
-
-def test_reduce_rejects_bad_arguments_before_launch(lib):
-    f = lib.pa_decode_reduce
-    # single partition: nothing to combine, nothing enqueued
-    assert f(16, 16, 1, 4, 4, 64, 50, 0, F16, None, 0, None) == OK
-    assert f(16, None, 1, 4, 4, 64, 600, 0, F16, 16, 1 << 20, None) == NULLP
-    assert f(16, 16, 1, 4, 4, 64, 600, 0, F16, 16, 10, None) == WS
-    assert f(16, 16, 1, 6, 4, 64, 600, 0, F16, 16, 1 << 20, None) == SHAPE
-    assert f(16, 16, 1, 4, 4, 64, 600, 8, F16, 16, 1 << 20, None) == SHAPE
-
-
-def test_partitions_entry_validates_like_decode(lib):
-    a = [16] * 6 + [0.125, 1, 4, 4, 64, 16, 4, 4, 50, 0, F32, None, 0, None]
-    bad = list(a)
-    bad[1] = None
-    assert lib.pa_decode_partitions(*bad) == NULLP
-    bad = list(a)
-    bad[14] = 65
-    assert lib.pa_decode_partitions(*bad) == SHAPE

@@ -147,7 +147,8 @@ SHAPES = [
     # dtype, Hq, Hkv, D, B
     ("f16", 8, 8, 128, 16), ("bf16", 8, 2, 128, 16), ("f32", 4, 4, 64, 16),
     ("f16", 8, 1, 64, 8), ("bf16", 16, 2, 64, 32), ("f16", 4, 2, 256, 64),
-    ("f32", 8, 4, 128, 32), ("bf16", 2, 2, 256, 8), ("f32", 8, 1, 256, 16),
+    ("f32", 8, 4, 128, 32), ("bf16", 2, 2, 256, 8), ("f32", 8, 1, 128, 16),
+    ("f16", 32, 4, 128, 32),
 ]
 EDGE_LENS = [1, 2, 15, 16, 17, 31, 33, 63, 64, 65, 255, 256, 257, 511, 513, 1000]
 
@@ -167,12 +168,13 @@ def test_shapes_and_ragged_lengths(dtype, hq, hkv, d, bs):
 
 
 def test_long_context_max_partition():
-    """A 65536-token sequence (longest tested), default and largest partition."""
+    """A 65536-token sequence (longest tested), default and largest partition
+    (64 blocks of 16 tokens)."""
     lens = np.array([65536, 3], np.int32)
     b = layouts.make_paged_batch(num_q_heads=8, num_kv_heads=8, head_dim=128, dtype="f16",
                                  block_size=16, context_lens=lens, seed=22, poison=False)
     _, _, o64 = oracle_step(b)
-    for partition in (0, 2048):
+    for partition in (0, 1024):
         _, out = gpu_step(b, partition=partition)
         assert_decode_close(layouts.from_device(out, "f16"), o64, "f16", f"64K P={partition}")
 
@@ -243,9 +245,9 @@ def test_gqa_matches_repeated_mha():
 
 
 def test_split_matches_unsplit():
-    b = layouts.scaled_config(4, max_seqs=1, max_len=2000)
+    b = layouts.scaled_config(4, max_seqs=1, max_len=1000)
     _, _, o64 = oracle_step(b)
-    _, whole = gpu_step(b, partition=2048)
+    _, whole = gpu_step(b, partition=1024)
     _, split = gpu_step(b, partition=16)
     for name, o in (("whole", whole), ("split", split)):
         assert_decode_close(layouts.from_device(o, "f16"), o64, "f16", name)
@@ -283,16 +285,99 @@ def test_out_of_range_table_entry_is_caught_in_debug_mode(monkeypatch):
     assert e.value.code == 6
 
 
-def test_two_launch_split_equals_decode():
-    """pa_decode_partitions then pa_decode_reduce is pa_decode, bit for bit."""
-    b = layouts.scaled_config(2, max_seqs=4, max_len=700)
-    t, whole = gpu_step(b, partition=64)
-    out = torch.empty_like(t["q"])
-    ws = torch.empty(ops.workspace_size(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
-                                        b.max_context_len, t["q"].dtype, 64),
-                     dtype=torch.uint8, device="cuda")
-    ops.decode_partitions(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
-                          t["context_lens"], b.scale, b.max_context_len, out, ws, 64)
-    ops.decode_reduce(out, t["context_lens"], b.num_kv_heads, b.max_context_len, ws, 64)
+def test_balanced_and_fixed_forms_agree():
+    """The balanced single launch and fixed partitions (two launches) both meet
+    the oracle, and agree with each other to float32 rounding."""
+    b = layouts.scaled_config(3, max_seqs=4, max_len=700, poison=True)
+    _, _, o64 = oracle_step(b)
+    t = layouts.to_device(b)
+    ops.reshape_and_cache(t["new_key"], t["new_value"], t["k_cache"], t["v_cache"],
+                          t["slot_mapping"])
+    outs = {}
+    for partition in (0, 64, 512):
+        outs[partition] = ops.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                     t["context_lens"], b.scale, b.max_context_len,
+                                     partition=partition)
     torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16), whole.view(torch.int16))
+    for partition, o in outs.items():
+        assert_decode_close(layouts.from_device(o, "bf16"), o64, "bf16", f"P={partition}")
+    diff = (outs[0].float() - outs[64].float()).abs().max().item()
+    assert diff <= 8e-3, diff
+
+
+def _counters(ws, num_items):
+    return ws[:4 * num_items].view(torch.int32)
+
+
+def test_balanced_form_reuses_its_workspace():
+    """Back-to-back calls on one workspace give bit-identical outputs, and the
+    arrival counters are zero again after every call (PA_DEBUG also checks
+    them on entry)."""
+    b = layouts.scaled_config(2, max_seqs=4, max_len=700)
+    t = layouts.to_device(b)
+    ws = ops.new_workspace(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                           b.max_context_len, t["q"].dtype, "cuda")
+    outs = []
+    for _ in range(3):
+        outs.append(ops.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                               t["context_lens"], b.scale, b.max_context_len, workspace=ws))
+        torch.cuda.synchronize()
+        assert int(_counters(ws, b.num_seqs * b.num_kv_heads).abs().sum()) == 0
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+def test_balanced_form_tiny_work_split_across_many_workgroups():
+    """16 tiles in all: most workgroups get no tile, each head is split over
+    several workgroups and combined by the last one."""
+    b = layouts.make_config(1, poison=True)
+    _, _, o64 = oracle_step(b)
+    _, out = gpu_step(b)
+    assert_decode_close(layouts.from_device(out, "f32"), o64, "f32", "tiny balanced")
+
+
+def test_balanced_form_many_sequences_and_empty_ones():
+    """600 sequences (the plan's prefix sum spans several chunks), some of
+    length 0 (zero rows), then more than 4096 sequences (fixed-partition
+    fallback). The step's cache write lands first (its slots start poisoned)."""
+    rng = np.random.default_rng(31)
+    lens = rng.integers(1, 120, size=600).astype(np.int32)
+    b = layouts.make_paged_batch(num_q_heads=4, num_kv_heads=2, head_dim=64, dtype="f16",
+                                 block_size=16, context_lens=lens, seed=32, poison=True)
+    kc, vc, _ = oracle_step(b, seqs=[0])
+    t = layouts.to_device(b)
+    ops.reshape_and_cache(t["new_key"], t["new_value"], t["k_cache"], t["v_cache"],
+                          t["slot_mapping"])
+    empty = [0, 17, 599]
+    t["context_lens"][empty] = 0
+    out = ops.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                     b.scale, b.max_context_len)
+    torch.cuda.synchronize()
+    keep = np.setdiff1d(np.arange(600), empty)
+    o64 = O.ref_decode(b.q[keep], kc, vc, b.block_tables[keep], b.context_lens[keep], b.scale,
+                       "f16")
+    got = layouts.from_device(out, "f16")
+    assert_decode_close(got[keep], o64, "f16", "600 seqs")
+    assert not got[empty].any()
+
+    lens = rng.integers(1, 40, size=4100).astype(np.int32)
+    b = layouts.make_paged_batch(num_q_heads=1, num_kv_heads=1, head_dim=64, dtype="f16",
+                                 block_size=16, context_lens=lens, seed=33, poison=True)
+    _, _, o64 = oracle_step(b)
+    _, out = gpu_step(b)
+    assert_decode_close(layouts.from_device(out, "f16"), o64, "f16", "4100 seqs")
+
+
+def test_long_rounds_and_windows():
+    """Chunks of many rounds per wave and segments longer than one window
+    (252 tiles for 16-token blocks, 128 for 8-token blocks), both forms."""
+    for bs, hkv, lens in ((16, 2, [4100, 700, 33]), (8, 2, [2100, 515]), (32, 4, [5000, 1])):
+        b = layouts.make_paged_batch(num_q_heads=2 * hkv, num_kv_heads=hkv, head_dim=128,
+                                     dtype="f16", block_size=bs,
+                                     context_lens=np.array(lens, np.int32), seed=40 + bs,
+                                     poison=True)
+        _, _, o64 = oracle_step(b)
+        for partition in (0, 512, 4096):
+            _, out = gpu_step(b, partition=partition)
+            assert_decode_close(layouts.from_device(out, "f16"), o64, "f16",
+                                f"B{bs} P={partition}")
