@@ -129,29 +129,40 @@ int32_t sync_copy_to_host(void *dst, const void *src, size_t bytes, hipStream_t 
 
 namespace pa {
 
-int flat_grid_size(const void *kernel, int threads, size_t dynamic_lds) {
+int flat_grid_size(const void *kernel, int threads, size_t dynamic_lds, int64_t max_tiles) {
   static std::mutex mu;
-  static std::map<std::tuple<int, const void *, size_t>, int> cache;
+  static std::map<std::tuple<int, const void *, size_t>, std::pair<int, int>> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   const auto key = std::make_tuple(dev, kernel, dynamic_lds);
-  std::lock_guard<std::mutex> lock(mu);
-  auto it = cache.find(key);
-  if (it != cache.end()) return it->second;
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return -1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dynamic_lds) !=
-      hipSuccess)
-    return -1;
-  if (const char *e = std::getenv("PA_FLAT_WGS_PER_CU")) {  // tuning knob
-    const int v = std::atoi(e);
-    if (v > 0) per_cu = v;
+  int cus = 0, resident = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) {
+      cus = it->second.first;
+      resident = it->second.second;
+    } else {
+      int per_cu = 0;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return -1;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dynamic_lds) !=
+          hipSuccess)
+        return -1;
+      if (const char *e = std::getenv("PA_FLAT_WGS_PER_CU")) {  // tuning knob
+        const int v = std::atoi(e);
+        if (v > 0) per_cu = v;
+      }
+      resident = cus * (per_cu > 0 ? per_cu : 1);
+      if (resident > kMaxFlatWorkgroups) resident = kMaxFlatWorkgroups;
+      cache[key] = std::make_pair(cus, resident);
+    }
   }
-  int grid = cus * (per_cu > 0 ? per_cu : 1);
-  if (grid > kMaxFlatWorkgroups) grid = kMaxFlatWorkgroups;
-  cache[key] = grid;
-  return grid;
+  // Small calls: fewer, longer ranges (each workgroup has a fixed start-up cost
+  // and a split (sequence, KV head) costs a combine).
+  int64_t want = (max_tiles + kMinFlatTiles - 1) / kMinFlatTiles;
+  if (want < cus) want = cus;
+  return want < resident ? int(want) : resident;
 }
 
 }  // namespace pa

@@ -32,7 +32,9 @@
 //   KB per wave in flight: the path is bound by HBM reads, not arithmetic.
 // * QK^T on the matrix cores (v_mfma 16x16x32 f16/bf16, 16x16x4 f32). Operand
 //   A is the K tile (row m = a token, loaded as 16 rows x 64 bytes per load),
-//   operand B the group's queries (column n = query head n % G). The tile's
+//   operand B the group's queries (column n = query head n % G), staged in LDS
+//   once per segment rather than held in registers (fewer VGPRs: GQA-4 runs
+//   three waves per SIMD instead of two). The tile's
 //   tokens are assigned to A rows through a fixed permutation chosen so that
 //   result slot i of lane l is the score of exactly the token whose V row
 //   segment lane l loads in V load i: scores never cross lanes for MHA.
@@ -215,7 +217,7 @@ template <int DT, int D, int G, int NT> struct SoftState {
 
 template <bool MASK, int DT, int D, int G, int NT>
 __device__ __forceinline__ void consume_round(const RoundBuf<DT, D, G, NT> &R,
-                                              SoftState<DT, D, G, NT> &st, const u32x4 *qb,
+                                              SoftState<DT, D, G, NT> &st, const u32x4 (*qb)[D * 4 / 16],
                                               float scale_log2, int rtok, int p_end) {
   using S = DecodeShape<DT, D, G, NT>;
   const int lane = __lane_id();
@@ -228,7 +230,7 @@ __device__ __forceinline__ void consume_round(const RoundBuf<DT, D, G, NT> &R,
   for (int t = 0; t < NT; ++t) {
     f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int s = 0; s < S::KS; ++s) a = mfma_chunk<DT>(R.k[t][s], qb[s], a);
+    for (int s = 0; s < S::KS; ++s) a = mfma_chunk<DT>(R.k[t][s], qb[(lane & 15) % G][(lane >> 4) + 4 * s], a);
 #pragma unroll
     for (int i = 0; i < S::VI; ++i) {
       float v;
@@ -302,6 +304,7 @@ template <int G, int D> struct MergeLds {
   float acc[kWaves][G][D];
   float m[kWaves][G];
   float l[kWaves][G];
+  u32x4 q[G][D * 4 / 16];  // the group's query rows in 16-byte chunks (room for f32 rows)
 };
 
 // Tiles of a wave's chunk inside one window: at most 64 blocks of table.
@@ -335,14 +338,18 @@ __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int 
     c.voff = (lane / S::LPT) * S::ROWB + (lane % S::LPT) * 16;
   }
 
-  // MFMA operand B: lane l holds query head (l % 16) % G, chunk (l / 16) + 4 s.
-  u32x4 qb[S::KS];
+  // MFMA operand B (lane l: query head (l % 16) % G, chunk (l / 16) + 4 s) is
+  // read from LDS: the group's query rows are staged there once per segment.
   {
-    const int head = kh * G + ((lane & 15) % G);
-    const char *qrow = reinterpret_cast<const char *>(p.q) + ((int64_t)seq * num_q_heads + head) * S::ROWB;
-#pragma unroll
-    for (int s = 0; s < S::KS; ++s) qb[s] = load_chunk(qrow, ((lane >> 4) + 4 * s) * 16);
+    const int tid = threadIdx.x;
+    const char *qrow0 = reinterpret_cast<const char *>(p.q) + ((int64_t)seq * num_q_heads + kh * G) * S::ROWB;
+    for (int i = tid; i < G * (S::ROWB / 16); i += kThreads) {
+      const int h = i / (S::ROWB / 16), ch = i % (S::ROWB / 16);
+      lds.q[h][ch] = load_chunk(qrow0, (int64_t)h * S::ROWB + ch * 16);
+    }
+    __syncthreads();
   }
+  const u32x4 (*qb)[D * 4 / 16] = lds.q;
 
   SoftState<DT, D, G, NT> st;
   st.m = -INFINITY;
@@ -723,7 +730,9 @@ static hipError_t launch_flat(const DecodeParams &p, hipStream_t stream) {
   constexpr int NT = rounds_tiles<DT, D, G>();
   auto kern = decode_flat_kernel<DT, D, G, NT, BS8>;
   const size_t shmem = flat_plan_lds_bytes(p.num_seqs);
-  const int grid = flat_grid_size(reinterpret_cast<const void *>(kern), kThreads, shmem);
+  const int64_t max_tiles =
+      (int64_t)p.num_seqs * p.num_kv_heads * ((p.max_context_len + 15) / 16);
+  const int grid = flat_grid_size(reinterpret_cast<const void *>(kern), kThreads, shmem, max_tiles);
   if (grid <= 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), shmem, stream, p);
   return hipGetLastError();

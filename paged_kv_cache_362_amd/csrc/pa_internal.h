@@ -66,7 +66,11 @@ hipError_t launch_reshape_and_cache(const CacheParams &p, hipStream_t stream);
 inline size_t flat_plan_lds_bytes(int num_seqs) { return size_t(2 * num_seqs + 1) * sizeof(int); }
 
 // Workgroups of a balanced launch on the current device: as many as can be
-// resident at once (capped at kMaxFlatWorkgroups). Defined in pa_api.cpp.
-int flat_grid_size(const void *kernel, int threads, size_t dynamic_lds);
+// resident at once (capped at kMaxFlatWorkgroups), but no more than give each
+// kMinFlatTiles of `max_tiles` (an upper bound of the call's 16-token tiles,
+// from max_context_len), and at least one per compute unit. Defined in
+// pa_api.cpp.
+constexpr int kMinFlatTiles = 64;
+int flat_grid_size(const void *kernel, int threads, size_t dynamic_lds, int64_t max_tiles);
 
 }  // namespace pa
