@@ -4,18 +4,21 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
 
 A step is the whole hot path over one batch: the cache write of the batch's
-new tokens (pa_reshape_and_cache) and the decode (pa_decode, balanced form: a
-single launch that also combines split heads). The default workload is the
-LLaMA-7B-layer MHA decode: 32 sequences, 32/32 heads of dim 128, fp16, 16-token
-blocks, context lengths uniform in [128, 2048], scattered over a shuffled pool
-with 25% slack. Inputs are seeded synthetic data already resident in HBM.
+new tokens and the attention over the paged cache. By default it is one launch
+(pa_decode_step: write and attention fused, balanced schedule); --separate
+times the two calls pa_reshape_and_cache + pa_decode instead. The default
+workload is the LLaMA-7B-layer MHA decode: 32 sequences, 32/32 heads of dim
+128, fp16, 16-token blocks, context lengths uniform in [128, 2048], scattered
+over a shuffled pool with 25% slack. Inputs are seeded synthetic data already
+resident in HBM.
 
 Timing: W untimed warm-up steps, then K timed steps. Before each step a 1 GiB
 buffer is read (outside the timed events) so the KV pools are not served from
 the 256 MB last-level cache; a read leaves no dirty lines behind, so the step
 is not charged for writing back the flush. Each step is bracketed by HIP events
-recorded on the stream the kernels run on, with an event between its two
-launches, so each kernel's duration is measured live. Prints one JSON line.
+recorded on the stream the kernels run on (with an event between the two
+launches of --separate), so each kernel's duration is measured live. Prints
+one JSON line.
 """
 
 from __future__ import annotations
@@ -47,6 +50,8 @@ def parse_args(argv=None):
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--partition", type=int, default=0,
                     help="0 = balanced single launch (default); >0 = fixed partitions")
+    ap.add_argument("--separate", action="store_true",
+                    help="time pa_reshape_and_cache + pa_decode (two launches) as the step")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -63,11 +68,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(config: int, partition: int):
-    """HBM bytes per partition-kernel launch from the committed counter profile.
+def stored_traffic(config: int, partition: int, fused: bool):
+    """HBM bytes per launch of the timed decode kernel, from the committed
+    counter profile.
 
-    Returns None unless the profile was taken on this workload with the
-    current kernel sources.
+    Returns None unless the profile was taken on this workload and form with
+    the current kernel sources.
     """
     path = os.path.join(ROOT, TRAFFIC_PROFILE)
     if not os.path.exists(path):
@@ -77,7 +83,7 @@ def stored_traffic(config: int, partition: int):
         return None
     rec = json.loads(m.group(1))
     if (rec.get("source_hash") != kernel_source_hash() or rec.get("config") != config
-            or rec.get("partition") != partition):
+            or rec.get("partition") != partition or rec.get("fused", False) != fused):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -158,15 +164,22 @@ def main(argv=None) -> int:
     ws = ops.new_workspace(s, hq, hkv, d, b.max_context_len, tdtype, dev, part)
     flush = None if args.no_flush else torch.ones(1 << 28, dtype=torch.float32, device=dev)
 
+    fused = not args.separate and part == 0
+
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        ops.reshape_and_cache(t["new_key"], t["new_value"], t["k_cache"], t["v_cache"],
-                              t["slot_mapping"])
-        if ev is not None:
-            ev[1].record()
-        ops.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
-                   b.scale, b.max_context_len, out, ws, part)
+        if fused:  # one launch: no event between (an event record costs the timeline ~us)
+            ops.decode_step(t["q"], t["new_key"], t["new_value"], t["k_cache"], t["v_cache"],
+                            t["slot_mapping"], t["block_tables"], t["context_lens"], b.scale,
+                            b.max_context_len, out, ws)
+        else:
+            ops.reshape_and_cache(t["new_key"], t["new_value"], t["k_cache"], t["v_cache"],
+                                  t["slot_mapping"])
+            if ev is not None:
+                ev[1].record()
+            ops.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                       t["context_lens"], b.scale, b.max_context_len, out, ws, part)
         if ev is not None:
             ev[2].record()
 
@@ -187,8 +200,9 @@ def main(argv=None) -> int:
     wall = time.perf_counter() - wall0
 
     step_ms = np.array([e[0].elapsed_time(e[2]) for e in events])
-    cache_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    # fused: the one launch; separate: the cache write, then the decode
+    first_ms = step_ms if fused else np.array([e[0].elapsed_time(e[1]) for e in events])
+    dec_ms = step_ms if fused else np.array([e[1].elapsed_time(e[2]) for e in events])
 
     e = b.elem_bytes
     lens = b.context_lens
@@ -198,9 +212,10 @@ def main(argv=None) -> int:
     kv_bytes = sizing.kv_read_bytes(lens, hkv, d, e)
     ms = float(step_ms.mean())
     value = step_bytes / (ms * 1e-3) / 1e9
-    achieved = decode_bytes / (float(dec_ms.mean()) * 1e-3) / 1e9
+    kernel_bytes = step_bytes if fused else decode_bytes
+    achieved = kernel_bytes / (float(dec_ms.mean()) * 1e-3) / 1e9
 
-    traffic = stored_traffic(args.config, part)
+    traffic = stored_traffic(args.config, part, fused)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -219,14 +234,17 @@ def main(argv=None) -> int:
             "num_kv_heads": hkv, "head_dim": d, "block_size": b.block_size,
             "context_tokens": int(lens.sum()), "max_context_len": b.max_context_len,
             "num_blocks": b.num_blocks,
-            "decode_form": "balanced" if part == 0 else f"fixed partitions of {part}",
+            "decode_form": ("balanced" if part == 0 else f"fixed partitions of {part}") +
+                           (", cache write fused (pa_decode_step)" if fused
+                            else ", cache write separate (pa_reshape_and_cache)"),
             "parallelism": "none (1 GPU)",
             "cache_flush_between_steps": flush is not None,
         },
         "pct_hbm_peak": round(100 * value / sizing.HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(s / (ms * 1e-3), 1),
         "kv_read_GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
-        "kernel_ms": {"reshape_and_cache": round(float(cache_ms.mean()), 5),
+        "kernel_ms": {("decode_step" if fused else "reshape_and_cache"):
+                      round(float(first_ms.mean()), 5),
                       "decode": round(float(dec_ms.mean()), 5),
                       "decode_median": round(float(np.median(dec_ms)), 5),
                       "step_median": round(float(np.median(step_ms)), 5),

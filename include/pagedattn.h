@@ -161,6 +161,39 @@ int32_t pa_decode(void *out, const void *q, const void *k_cache,
                   int32_t partition_size, int32_t dtype, void *workspace,
                   size_t workspace_bytes, void *stream);
 
+/*
+ * pa_decode_step - one whole decode step in a single launch: the cache write of
+ * this step's tokens, then the attention (a decode step appends the new
+ * token's K and V to the cache and attends over everything cached,
+ * [INFRA] §1.2).
+ *
+ * Same result as pa_reshape_and_cache(key, value, k_cache, v_cache,
+ * slot_mapping, num_seqs, ...) followed by pa_decode(..., partition_size = 0,
+ * ...): the pools end with the new rows in place and `out` is bit-identical.
+ * Token s of key/value [num_seqs, num_kv_heads, head_dim] belongs to sequence
+ * s and must be its last attended position: for context_lens[s] >= 1 and
+ * slot_mapping[s] >= 0, slot_mapping[s] must be the slot of position
+ * context_lens[s] - 1 (table entry (n-1)/block_size, offset (n-1)%block_size),
+ * checked under PA_DEBUG only. slot_mapping[s] < 0 writes nothing for that
+ * sequence (its last position is then read from the pools).
+ *
+ * The attention reads the new rows from key/value, not from the pools, so the
+ * write and the reads need no ordering inside the launch. Workspace as for
+ * pa_decode with partition_size 0 (zero-filled before its first use). Beyond
+ * 4096 sequences the call writes first and then decodes with fixed partitions
+ * (two launches).
+ */
+int32_t pa_decode_step(void *out, const void *q, const void *key,
+                       const void *value, void *k_cache, void *v_cache,
+                       const int32_t *slot_mapping, const int32_t *block_tables,
+                       const int32_t *context_lens, float scale,
+                       int32_t num_seqs, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks,
+                       int32_t max_blocks_per_seq, int32_t max_context_len,
+                       int32_t dtype, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
 /* A static, human-readable name of a status code. */
 const char *pa_status_str(int32_t status);
 

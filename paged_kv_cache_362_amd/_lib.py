@@ -23,6 +23,9 @@ SIGNATURES = {
     "pa_decode_workspace_size": (_size, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _f32, _i32, _i32, _i32, _i32, _i32,
                          _i32, _i32, _i32, _i32, _i32, _ptr, _size, _ptr]),
+    "pa_decode_step": (_i32, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _f32, _i32,
+                              _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _ptr, _size,
+                              _ptr]),
     "pa_status_str": (ctypes.c_char_p, [_i32]),
     "pa_abi_version": (_i32, []),
 }

@@ -235,12 +235,26 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
       .total;
 }
 
-int32_t pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
-                  const int32_t *block_tables, const int32_t *context_lens, float scale,
-                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                  int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size,
-                  int32_t dtype, void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// This step's new tokens (decode step form), or all null.
+struct StepArgs {
+  const void *key = nullptr;
+  const void *value = nullptr;
+  void *k_cache = nullptr;
+  void *v_cache = nullptr;
+  const int32_t *slot_mapping = nullptr;
+};
+
+int32_t decode_impl(void *out, const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, const int32_t *context_lens, float scale,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                    int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size,
+                    int32_t dtype, void *workspace, size_t workspace_bytes, void *stream,
+                    const StepArgs &step) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int32_t st = check_decode_shapes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                    max_context_len, dtype);
@@ -257,6 +271,11 @@ int32_t pa_decode(void *out, const void *q, const void *k_cache, const void *v_c
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return PA_ERR_NULL_POINTER;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
+  const bool fused = step.slot_mapping != nullptr;
+  if (fused) {
+    if (!step.key || !step.value) return PA_ERR_NULL_POINTER;
+    if (!aligned16(step.key) || !aligned16(step.value)) return PA_ERR_UNSUPPORTED;
+  }
   const WsLayout lay = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                         max_context_len, partition_size);
   const int32_t max_parts = balanced ? 1 : num_partitions(max_context_len, part);
@@ -266,6 +285,7 @@ int32_t pa_decode(void *out, const void *q, const void *k_cache, const void *v_c
     if (workspace_bytes < lay.total) return PA_ERR_WORKSPACE_TOO_SMALL;
     if (!aligned16(workspace)) return PA_ERR_UNSUPPORTED;
   }
+  const int64_t num_slots = int64_t(num_blocks) * block_size;
 
   if (debug_checks()) {
     std::vector<int32_t> lens(num_seqs);
@@ -283,6 +303,23 @@ int32_t pa_decode(void *out, const void *q, const void *k_cache, const void *v_c
         if (b < 0 || b >= num_blocks) return PA_ERR_BAD_INDEX;
       }
     }
+    if (fused) {  // each new token is the last position of its sequence
+      std::vector<int32_t> slots(num_seqs);
+      st = sync_copy_to_host(slots.data(), step.slot_mapping, sizeof(int32_t) * slots.size(), s);
+      if (st != PA_OK) return st;
+      std::unordered_set<int32_t> seen;
+      for (int32_t i = 0; i < num_seqs; ++i) {
+        const int32_t v = slots[i];
+        if (v < 0) continue;
+        if (v >= num_slots || !seen.insert(v).second) return PA_ERR_BAD_INDEX;
+        const int32_t n = lens[i];
+        if (n < 1) continue;
+        const int32_t last = n - 1;
+        const int32_t want = tab[size_t(i) * max_blocks_per_seq + last / block_size] * block_size +
+                             last % block_size;
+        if (v != want) return PA_ERR_BAD_INDEX;
+      }
+    }
     if (balanced) {  // the arrival counters must be zero
       std::vector<int32_t> cnt(size_t(num_seqs) * num_kv_heads);
       st = sync_copy_to_host(cnt.data(), workspace, sizeof(int32_t) * cnt.size(), s);
@@ -290,6 +327,14 @@ int32_t pa_decode(void *out, const void *q, const void *k_cache, const void *v_c
       for (int32_t c : cnt)
         if (c != 0) return PA_ERR_BAD_INDEX;
     }
+  }
+
+  if (fused && !balanced) {
+    // Fixed partitions cannot take the new rows from LDS: write them first.
+    st = pa_reshape_and_cache(step.key, step.value, step.k_cache, step.v_cache,
+                              step.slot_mapping, num_seqs, num_kv_heads, head_dim, block_size,
+                              num_blocks, dtype, stream);
+    if (st != PA_OK) return st;
   }
 
   pa::DecodeParams p{};
@@ -318,8 +363,52 @@ int32_t pa_decode(void *out, const void *q, const void *k_cache, const void *v_c
   p.partition_size = balanced ? 0 : part;
   p.max_partitions = max_parts;
   p.dtype = dtype;
+  if (fused && balanced) {
+    p.new_key = step.key;
+    p.new_value = step.value;
+    p.slot_mapping = step.slot_mapping;
+    p.k_cache_w = step.k_cache;
+    p.v_cache_w = step.v_cache;
+    p.num_slots = num_slots;
+  }
   const pa::DecodeStage stage = balanced ? pa::kStageFlat : pa::kStageBoth;
   return pa::launch_decode(p, s, stage) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                  const int32_t *block_tables, const int32_t *context_lens, float scale,
+                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                  int32_t max_blocks_per_seq, int32_t max_context_len, int32_t partition_size,
+                  int32_t dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, partition_size, dtype, workspace,
+                     workspace_bytes, stream, StepArgs{});
+}
+
+int32_t pa_decode_step(void *out, const void *q, const void *key, const void *value,
+                       void *k_cache, void *v_cache, const int32_t *slot_mapping,
+                       const int32_t *block_tables, const int32_t *context_lens, float scale,
+                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                       int32_t max_blocks_per_seq, int32_t max_context_len, int32_t dtype,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+  if (num_seqs > 0 && !slot_mapping) return PA_ERR_NULL_POINTER;
+  StepArgs step;
+  step.key = key;
+  step.value = value;
+  step.k_cache = k_cache;
+  step.v_cache = v_cache;
+  step.slot_mapping = slot_mapping;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, 0, dtype, workspace, workspace_bytes,
+                     stream, step);
 }
 
 }  // extern "C"

@@ -215,6 +215,40 @@ template <int DT, int D, int G, int NT> struct SoftState {
   float acc[G][S::NSEG][S::EPC];
 };
 
+// The row of the token written in this decode step, staged in LDS.
+struct NewRow {
+  int pos;            // its position in the sequence, or -1 when there is none
+  const u32x4 *k;     // 16-byte chunks of its K row (this KV head)
+  const u32x4 *v;
+};
+
+// Decode step: the position written this step takes its K/V from the staged
+// copy of the new row instead of the pool (another workgroup may be writing
+// that pool row right now). Only a chunk's last round can hold it.
+template <int DT, int D, int G, int NT>
+__device__ __forceinline__ void apply_new_row(RoundBuf<DT, D, G, NT> &R, const NewRow &nr,
+                                              int rtok) {
+  using S = DecodeShape<DT, D, G, NT>;
+  if (nr.pos < rtok || nr.pos >= rtok + S::ROUND) return;
+  const int lane = __lane_id();
+  const int ktok = tile_token_of_row<S::LPT>(lane & 15);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (rtok + 16 * t + ktok == nr.pos) {
+#pragma unroll
+      for (int s = 0; s < S::KS; ++s) R.k[t][s] = nr.k[(lane >> 4) + 4 * s];
+    }
+#pragma unroll
+    for (int i = 0; i < S::VI; ++i) {
+      if (rtok + 16 * t + i * S::TPI + lane / S::LPT == nr.pos) {
+#pragma unroll
+        for (int sg = 0; sg < S::NSEG; ++sg)
+          R.v[t][i * S::NSEG + sg] = nr.v[sg * (S::SEGB / 16) + lane % S::LPT];
+      }
+    }
+  }
+}
+
 template <bool MASK, int DT, int D, int G, int NT>
 __device__ __forceinline__ void consume_round(const RoundBuf<DT, D, G, NT> &R,
                                               SoftState<DT, D, G, NT> &st, const u32x4 (*qb)[D * 4 / 16],
@@ -305,6 +339,8 @@ template <int G, int D> struct MergeLds {
   float m[kWaves][G];
   float l[kWaves][G];
   u32x4 q[G][D * 4 / 16];  // the group's query rows in 16-byte chunks (room for f32 rows)
+  u32x4 newk[D * 4 / 16];  // decode step: this KV head's row of the token written this step
+  u32x4 newv[D * 4 / 16];
 };
 
 // Tiles of a wave's chunk inside one window: at most 64 blocks of table.
@@ -318,7 +354,8 @@ template <bool BS8> constexpr int chunk_tiles() { return BS8 ? 32 : 63; }
 // per head in LDS; the caller synchronises the workgroup before reading them.
 template <int DT, int D, int G, int NT, bool BS8>
 __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int kh, int p_start,
-                                            int p_end, int wave, MergeLds<G, D> &lds) {
+                                            int p_end, int wave, MergeLds<G, D> &lds,
+                                            int new_pos = -1) {
   using S = DecodeShape<DT, D, G, NT>;
   const int lane = __lane_id();
   const int num_q_heads = p.num_kv_heads * G;
@@ -347,8 +384,15 @@ __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int 
       const int h = i / (S::ROWB / 16), ch = i % (S::ROWB / 16);
       lds.q[h][ch] = load_chunk(qrow0, (int64_t)h * S::ROWB + ch * 16);
     }
+    if (new_pos >= 0 && tid < 2 * (S::ROWB / 16)) {  // decode step: stage the new row
+      const int ch = tid % (S::ROWB / 16);
+      const int64_t src = ((int64_t)seq * p.num_kv_heads + kh) * S::ROWB + ch * 16;
+      if (tid < S::ROWB / 16) lds.newk[ch] = load_chunk(p.new_key, src);
+      else lds.newv[ch] = load_chunk(p.new_value, src);
+    }
     __syncthreads();
   }
+  const NewRow new_row{new_pos, lds.newk, lds.newv};
   const u32x4 (*qb)[D * 4 / 16] = lds.q;
 
   SoftState<DT, D, G, NT> st;
@@ -397,8 +441,10 @@ __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int 
       load_round<BS8>(B, c, rtok_of(r + 1));
       __builtin_amdgcn_sched_barrier(0);
       consume_round<false>(A, st, qb, sl2, rtok_of(r), tok_end);
+      if (new_pos >= 0) apply_new_row(B, new_row, rtok_of(r + 1));
       consume_round<true>(B, st, qb, sl2, rtok_of(r + 1), tok_end);
     } else {
+      if (new_pos >= 0) apply_new_row(A, new_row, rtok_of(r));
       consume_round<true>(A, st, qb, sl2, rtok_of(r), tok_end);
     }
   }
@@ -556,10 +602,52 @@ __device__ __forceinline__ int wg_of_tile(int64_t x, int64_t total, int nwg) {
   return (int)(((x + 1) * nwg - 1) / total);
 }
 
-template <int DT, int D, int G, int NT, bool BS8>
+// Decode step: this step's K/V rows go into the pools one (sequence, KV head)
+// pair per workgroup in turn (pair i by workgroup i mod grid). Nothing in the
+// launch reads them back from the pools: the attention takes them from LDS
+// (see consume_round). A workgroup loads its first pair at the start, next to
+// the plan's loads, and stores it once the plan is done; further pairs (more
+// pairs than workgroups) are copied after its attention work.
+template <int DT, int D, int G> struct NewRowCopy {
+  static constexpr int kChunks = DecodeShape<DT, D, G, 1>::ROWB / 16;
+  u32x4 data;
+  int slot = -1;
+
+  __device__ __forceinline__ void load(const DecodeParams &p, int pair) {
+    const int tid = threadIdx.x;
+    if (pair < p.num_seqs * p.num_kv_heads && tid < 2 * kChunks) {
+      slot = p.slot_mapping[pair / p.num_kv_heads];
+      if (slot >= p.num_slots) slot = -1;  // out of range: nothing is written
+      const int64_t src = ((int64_t)pair * kChunks + tid % kChunks) * 16;
+      data = load_chunk(tid < kChunks ? p.new_key : p.new_value, src);
+    }
+  }
+  __device__ __forceinline__ void store(const DecodeParams &p, int pair) const {
+    const int tid = threadIdx.x;
+    if (slot < 0) return;
+    const int kh = pair % p.num_kv_heads;
+    const int bshift = p.block_shift;
+    const int64_t row = (((int64_t)(slot >> bshift) * p.num_kv_heads + kh) << bshift) +
+                        (slot & ((1 << bshift) - 1));
+    const int64_t dst = (row * kChunks + tid % kChunks) * 16;
+    store_chunk(tid < kChunks ? p.k_cache_w : p.v_cache_w, dst, data);
+  }
+};
+
+// Pairs first, first + grid, ... (the ones past a workgroup's first).
+template <int DT, int D, int G>
+__device__ __forceinline__ void copy_new_rows(const DecodeParams &p, int first) {
+  for (int pair = first; pair < p.num_seqs * p.num_kv_heads; pair += gridDim.x) {
+    NewRowCopy<DT, D, G> row;
+    row.load(p, pair);
+    row.store(p, pair);
+  }
+}
+
+template <int DT, int D, int G, int NT, bool BS8, bool STEP>
 __global__ __launch_bounds__(kThreads) void decode_flat_kernel(DecodeParams p) {
   using OutT = typename Store<DT>::T;
-  extern __shared__ int s_plan[];  // tiles prefix [S + 1], clamped lengths [S]
+  extern __shared__ int s_plan[];  // tiles prefix [S + 1], clamped lengths [S], slots [S]
   __shared__ MergeLds<G, D> lds;
   __shared__ int s_wsum[kWaves];
   __shared__ int s_found;
@@ -574,7 +662,11 @@ __global__ __launch_bounds__(kThreads) void decode_flat_kernel(DecodeParams p) {
   const int w = blockIdx.x;
   int *s_tc = s_plan;
   int *s_n = s_plan + S + 1;
+  int *s_slot = s_n + S;  // decode step: this step's slot per sequence (-1: none)
   OutT *out = reinterpret_cast<OutT *>(p.out);
+
+  NewRowCopy<DT, D, G> first_row;
+  if (STEP) first_row.load(p, w);
 
   // Plan: tiles per sequence and their prefix sums (every workgroup computes the
   // same plan from context_lens).
@@ -601,11 +693,15 @@ __global__ __launch_bounds__(kThreads) void decode_flat_kernel(DecodeParams p) {
     if (s < S) {
       s_tc[s + 1] = off + x;
       s_n[s] = n;
+      const int slot = STEP ? p.slot_mapping[s] : -1;
+      s_slot[s] = slot >= 0 && slot < p.num_slots ? slot : -1;
     }
     carry += total;
     __syncthreads();
   }
   const int64_t total = (int64_t)hkv * carry;
+
+  if (STEP) first_row.store(p, w);
 
   // Empty contexts: zero output rows, spread over the workgroups.
   for (int s = w; s < S; s += gridDim.x)
@@ -616,7 +712,10 @@ __global__ __launch_bounds__(kThreads) void decode_flat_kernel(DecodeParams p) {
   // With fewer tiles than workgroups only the first `total` take part, so every
   // range below is non-empty (the combine counts on that).
   const int nwg = (int)min((int64_t)gridDim.x, total);
-  if (w >= nwg) return;
+  if (w >= nwg) {
+    if (STEP) copy_new_rows<DT, D, G>(p, w + gridDim.x);
+    return;
+  }
   const int64_t start = (int64_t)w * total / nwg;
   const int64_t end = (int64_t)(w + 1) * total / nwg;
 
@@ -639,7 +738,9 @@ __global__ __launch_bounds__(kThreads) void decode_flat_kernel(DecodeParams p) {
     const int p_start = 16 * a;
     const int p_end = min(16 * b, n);
 
-    run_segment<DT, D, G, NT, BS8>(p, seq, kh, p_start, p_end, wave, lds);
+    int new_pos = -1;  // decode step: the written position, when this segment ends the item
+    if (STEP && b == tiles && s_slot[seq] >= 0) new_pos = n - 1;
+    run_segment<DT, D, G, NT, BS8>(p, seq, kh, p_start, p_end, wave, lds, new_pos);
     __syncthreads();
 
     const bool whole = a == 0 && b == tiles;
@@ -715,6 +816,7 @@ __global__ __launch_bounds__(kThreads) void decode_flat_kernel(DecodeParams p) {
     __syncthreads();  // lds and s_last are reused by the next segment
     pos = item_base + b;
   }
+  if (STEP) copy_new_rows<DT, D, G>(p, w + gridDim.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -725,10 +827,10 @@ template <int DT, int D, int G> constexpr int rounds_tiles() {
   return (D * Elem<DT>::kBytes) >= 256 ? 1 : 2;
 }
 
-template <int DT, int D, int G, bool BS8>
+template <int DT, int D, int G, bool BS8, bool STEP>
 static hipError_t launch_flat(const DecodeParams &p, hipStream_t stream) {
   constexpr int NT = rounds_tiles<DT, D, G>();
-  auto kern = decode_flat_kernel<DT, D, G, NT, BS8>;
+  auto kern = decode_flat_kernel<DT, D, G, NT, BS8, STEP>;
   const size_t shmem = flat_plan_lds_bytes(p.num_seqs);
   const int64_t max_tiles =
       (int64_t)p.num_seqs * p.num_kv_heads * ((p.max_context_len + 15) / 16);
@@ -742,8 +844,13 @@ template <int DT, int D, int G>
 static hipError_t launch_dtg(const DecodeParams &p, hipStream_t stream, DecodeStage stage) {
   constexpr int NT = rounds_tiles<DT, D, G>();
   const bool bs8 = p.block_shift == 3;
-  if (stage == kStageFlat)
-    return bs8 ? launch_flat<DT, D, G, true>(p, stream) : launch_flat<DT, D, G, false>(p, stream);
+  if (stage == kStageFlat) {
+    if (p.slot_mapping != nullptr)
+      return bs8 ? launch_flat<DT, D, G, true, true>(p, stream)
+                 : launch_flat<DT, D, G, false, true>(p, stream);
+    return bs8 ? launch_flat<DT, D, G, true, false>(p, stream)
+               : launch_flat<DT, D, G, false, false>(p, stream);
+  }
   if (stage != kStageReduce) {
     dim3 grid(p.max_partitions, p.num_kv_heads, p.num_seqs);
     if (bs8)

@@ -40,6 +40,15 @@ struct DecodeParams {
   int partition_size;
   int max_partitions;
   int dtype;
+  // Fused cache write (decode step form; null otherwise): token s of
+  // new_key/new_value [S, Hkv, D] goes to slot_mapping[s] of the pools, and is
+  // the last position (context_lens[s] - 1) of sequence s.
+  const void *new_key;
+  const void *new_value;
+  const int32_t *slot_mapping;
+  void *k_cache_w;
+  void *v_cache_w;
+  int64_t num_slots;
 };
 
 struct CacheParams {
@@ -62,8 +71,9 @@ enum DecodeStage { kStageBoth = 0, kStagePartitions = 1, kStageReduce = 2, kStag
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream, DecodeStage stage);
 hipError_t launch_reshape_and_cache(const CacheParams &p, hipStream_t stream);
 
-// Dynamic LDS of the balanced form's plan.
-inline size_t flat_plan_lds_bytes(int num_seqs) { return size_t(2 * num_seqs + 1) * sizeof(int); }
+// Dynamic LDS of the balanced form's plan: tile prefix sums [S + 1], clamped
+// lengths [S] and this step's slots [S].
+inline size_t flat_plan_lds_bytes(int num_seqs) { return size_t(3 * num_seqs + 1) * sizeof(int); }
 
 // Workgroups of a balanced launch on the current device: as many as can be
 // resident at once (capped at kMaxFlatWorkgroups), but no more than give each

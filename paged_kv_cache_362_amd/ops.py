@@ -148,3 +148,30 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     _launch_decode("pa_decode", q, k_cache, v_cache, block_tables, context_lens, scale,
                    max_context_len, out, workspace, partition)
     return out
+
+
+def decode_step(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                k_cache: torch.Tensor, v_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                max_context_len: int, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """One decode step in one launch: write key/value [S, Hkv, D] at slot_mapping
+    [S] (each the last position of its sequence), then paged attention."""
+    out, workspace = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                  max_context_len, out, workspace, 0)
+    _on_gpu(key, value, slot_mapping)
+    _require(key.shape == value.shape == (q.shape[0], k_cache.shape[1], q.shape[2]),
+             "key/value must be [S, Hkv, D]")
+    _require(key.dtype == value.dtype == q.dtype, "key/value share q's dtype")
+    _require(slot_mapping.dtype == torch.int32 and slot_mapping.shape == (q.shape[0],),
+             "slot_mapping must be int32 [S]")
+    s, hq, d = q.shape
+    n, hkv, bs, _ = k_cache.shape
+    code = lib().pa_decode_step(
+        _dev_ptr(out), _dev_ptr(q), _dev_ptr(key), _dev_ptr(value), _dev_ptr(k_cache),
+        _dev_ptr(v_cache), _dev_ptr(slot_mapping), _dev_ptr(block_tables),
+        _dev_ptr(context_lens), float(scale), s, hq, hkv, d, bs, n, block_tables.shape[1],
+        int(max_context_len), dtype_code(q.dtype), _dev_ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q))
+    _check("pa_decode_step", code)
+    return out

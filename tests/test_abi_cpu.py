@@ -32,8 +32,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("pa_reshape_and_cache", "pa_decode", "pa_decode_workspace_size", "pa_status_str",
-              "pa_abi_version"):
+    for n in ("pa_reshape_and_cache", "pa_decode", "pa_decode_step", "pa_decode_workspace_size",
+              "pa_status_str", "pa_abi_version"):
         assert n in names
 
 
@@ -120,3 +120,24 @@ def test_cache_write_rejects_bad_arguments_before_launch(lib):
     assert f(16, 16, 16, 16, 16, 1, 4, 64, 24, 8, F16, None) == UNSUP
     assert f(16, 16, 24, 16, 16, 1, 4, 64, 16, 8, F16, None) == UNSUP
     assert f(None, None, None, None, None, 0, 4, 64, 16, 8, F16, None) == OK
+
+
+def test_decode_step_rejects_bad_arguments_before_launch(lib):
+    f = lib.pa_decode_step
+
+    def call(**kw):
+        a = dict(out=16, q=16, key=16, value=16, k=16, v=16, slots=16, bt=16, cl=16,
+                 scale=0.125, S=1, Hq=4, Hkv=4, D=64, B=16, N=4, M=4, maxlen=50, dtype=F16,
+                 ws=16, wsb=1 << 22, stream=None)
+        a.update(kw)
+        return f(a["out"], a["q"], a["key"], a["value"], a["k"], a["v"], a["slots"], a["bt"],
+                 a["cl"], a["scale"], a["S"], a["Hq"], a["Hkv"], a["D"], a["B"], a["N"],
+                 a["M"], a["maxlen"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+    assert call(slots=None) == NULLP
+    assert call(key=None) == NULLP
+    assert call(value=24) == UNSUP  # misaligned
+    assert call(Hq=6) == SHAPE
+    assert call(maxlen=65) == SHAPE
+    assert call(ws=16, wsb=100) == WS
+    assert call(S=0, q=None, out=None, slots=None) == OK

@@ -381,3 +381,96 @@ def test_long_rounds_and_windows():
             _, out = gpu_step(b, partition=partition)
             assert_decode_close(layouts.from_device(out, "f16"), o64, "f16",
                                 f"B{bs} P={partition}")
+
+
+# ---------------------------------------------------------------------------
+# the fused decode step (cache write + attention in one launch)
+# ---------------------------------------------------------------------------
+
+def _two_calls(b, t):
+    ops.reshape_and_cache(t["new_key"], t["new_value"], t["k_cache"], t["v_cache"],
+                          t["slot_mapping"])
+    return ops.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                      b.scale, b.max_context_len)
+
+
+def _fused(b, t):
+    return ops.decode_step(t["q"], t["new_key"], t["new_value"], t["k_cache"], t["v_cache"],
+                           t["slot_mapping"], t["block_tables"], t["context_lens"], b.scale,
+                           b.max_context_len)
+
+
+def _same_bits(x, y):
+    if x.dtype == torch.float32:
+        return torch.equal(x.view(torch.int32), y.view(torch.int32))
+    return torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_decode_step_equals_write_then_decode(cfg):
+    """Same pools and bit-identical output as the two separate calls; the new
+    tokens' slots start poisoned, so reading them from the pools would show."""
+    b = layouts.scaled_config(cfg, poison=True, max_seqs=4, max_len=700)
+    _, _, o64 = oracle_step(b)
+    t1 = layouts.to_device(b)
+    t2 = layouts.to_device(b)
+    o_sep = _two_calls(b, t1)
+    o_fused = _fused(b, t2)
+    torch.cuda.synchronize()
+    assert _same_bits(o_sep, o_fused)
+    assert _same_bits(t1["k_cache"], t2["k_cache"]) and _same_bits(t1["v_cache"], t2["v_cache"])
+    assert_decode_close(layouts.from_device(o_fused, b.dtype), o64, b.dtype, f"step {b.name}")
+
+
+def test_decode_step_full_size_workload():
+    b = layouts.make_config(2, poison=True)
+    order = np.argsort(b.context_lens)
+    seqs = np.unique(np.concatenate([order[:2], order[-2:], [5, 17]]))
+    _, _, o64 = oracle_step(b, seqs)
+    t = layouts.to_device(b)
+    out = _fused(b, t)
+    torch.cuda.synchronize()
+    assert_decode_close(layouts.from_device(out, b.dtype)[seqs], o64, b.dtype, "step cfg2")
+    kc, _, _ = oracle_step(b, seqs=[0])
+    assert np.array_equal(layouts.from_device(t["k_cache"], "f16").view(np.int16),
+                          kc.view(np.int16))
+
+
+def test_decode_step_skipped_slots_and_empty_sequences():
+    """slot < 0: nothing written, the last position is read from the pool (as
+    the two calls do); a sequence of length 0 still gets its write."""
+    b = layouts.scaled_config(2, poison=False, max_seqs=4, max_len=300)
+    t1 = layouts.to_device(b)
+    t2 = layouts.to_device(b)
+    for t in (t1, t2):
+        t["slot_mapping"][1] = -1
+        t["context_lens"][3] = 0
+    o_sep = _two_calls(b, t1)
+    o_fused = _fused(b, t2)
+    torch.cuda.synchronize()
+    assert _same_bits(o_sep, o_fused)
+    assert torch.all(o_fused[3] == 0)
+    assert _same_bits(t1["k_cache"], t2["k_cache"]) and _same_bits(t1["v_cache"], t2["v_cache"])
+
+
+def test_decode_step_many_sequences_falls_back():
+    """More than 4096 sequences: write, then fixed partitions (two launches)."""
+    rng = np.random.default_rng(35)
+    lens = rng.integers(1, 40, size=4100).astype(np.int32)
+    b = layouts.make_paged_batch(num_q_heads=2, num_kv_heads=1, head_dim=64, dtype="f16",
+                                 block_size=16, context_lens=lens, seed=36, poison=True)
+    _, _, o64 = oracle_step(b)
+    t = layouts.to_device(b)
+    out = _fused(b, t)
+    torch.cuda.synchronize()
+    assert_decode_close(layouts.from_device(out, "f16"), o64, "f16", "step 4100 seqs")
+
+
+def test_decode_step_checks_slots_in_debug_mode(monkeypatch):
+    b = layouts.scaled_config(2, max_seqs=4, max_len=300)
+    t = layouts.to_device(b)
+    t["slot_mapping"][2] += 1  # not the last position any more
+    monkeypatch.setenv("PA_DEBUG", "1")
+    with pytest.raises(ops.PagedAttentionError) as e:
+        _fused(b, t)
+    assert e.value.code == 6
