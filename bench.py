@@ -57,6 +57,9 @@ def parse_args(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--paging-sweep", action="store_true",
+                    help="decode on contiguous vs shuffled block tables at block sizes "
+                         "8/16/32/64 (LLaMA-7B-layer shapes); prints one JSON line")
     return ap.parse_args(argv)
 
 
@@ -97,6 +100,67 @@ def calib_copy() -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
+
+
+def paging_sweep(args) -> dict:
+    """Cost of paging itself: the same decode over the same pool and lengths, with each
+    sequence's blocks contiguous in the pool (identity-ordered free list) or
+    scattered (shuffled), at every block size; plus the slots the last blocks
+    leave empty. The pages put the non-contiguous penalty under 5% ([INFRA]
+    FAQ) and the paged-vs-standard latency gap at 4-5% ([OPS])."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_362_amd import layouts, ops, sizing
+
+    dev = torch.device("cuda:0")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    spec = layouts.CONFIGS[2]
+    rows = []
+    for bs in (8, 16, 32, 64):
+        per_layout = {}
+        for shuffled in (False, True):
+            b = layouts.make_paged_batch(
+                num_q_heads=spec.num_q_heads, num_kv_heads=spec.num_kv_heads,
+                head_dim=spec.head_dim, dtype=spec.dtype, block_size=bs,
+                context_lens=lambda rng: layouts.config_context_lens(2, rng), seed=2,
+                shuffle_pool=shuffled)
+            t = layouts.to_device(b, dev)
+            out = torch.empty_like(t["q"])
+            ws = ops.new_workspace(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                                   b.max_context_len, t["q"].dtype, dev)
+
+            def call():
+                ops.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                           t["context_lens"], b.scale, b.max_context_len, out, ws)
+            for _ in range(args.warmup):
+                flush.amax()
+                call()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+            for e0, e1 in ev:
+                flush.amax()
+                e0.record()
+                call()
+                e1.record()
+            torch.cuda.synchronize()
+            ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+            nbytes = sizing.decode_algorithmic_bytes(b.context_lens, b.num_q_heads,
+                                                     b.num_kv_heads, b.head_dim, b.elem_bytes,
+                                                     bs)
+            per_layout["shuffled" if shuffled else "contiguous"] = {
+                "decode_us": round(ms * 1e3, 2), "GBps": round(nbytes / ms / 1e6, 1)}
+            frag = sizing.internal_fragmentation(b.context_lens, bs)
+            del t, out, ws
+            torch.cuda.empty_cache()
+        c, sh = per_layout["contiguous"]["decode_us"], per_layout["shuffled"]["decode_us"]
+        rows.append({"block_size": bs, **per_layout,
+                     "shuffled_vs_contiguous_pct": round(100 * (sh - c) / c, 2),
+                     "internal_fragmentation_pct": round(100 * frag, 2),
+                     "table_entries_per_2048_tokens": 2048 // bs})
+    return {"paging_sweep": rows,
+            "workload": "LLaMA-7B-layer MHA decode shapes (32 seqs, 32/32 heads, D 128, "
+                        "fp16, lengths U[128, 2048]), balanced pa_decode",
+            "steps": args.steps, "warmup": args.warmup, "statistic": "median"}
 
 
 def cpu_baseline(batch, seconds: float) -> dict:
@@ -145,6 +209,9 @@ def main(argv=None) -> int:
 
     if args.calib_copy:
         calib_copy()
+        return 0
+    if args.paging_sweep:
+        print(json.dumps(paging_sweep(args)), flush=True)
         return 0
 
     from paged_kv_cache_362_amd import layouts, ops, sizing

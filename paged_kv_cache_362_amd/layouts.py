@@ -182,6 +182,7 @@ def make_paged_batch(*, num_q_heads: int, num_kv_heads: int, head_dim: int, dtyp
                      num_blocks: int | None = None, pool_slack: float = 0.25,
                      shared_prefix_seqs: int = 0, shared_prefix_tokens: int = 0,
                      fresh_block_write: bool = False, extra_table_cols: int = 0,
+                     shuffle_pool: bool = True,
                      rng: np.random.Generator | None = None, name: str = "") -> PagedBatch:
     """Build one decode step's inputs.
 
@@ -190,7 +191,9 @@ def make_paged_batch(*, num_q_heads: int, num_kv_heads: int, head_dim: int, dtyp
     their first ``shared_prefix_tokens`` tokens (whole blocks) with sequence 0.
     With ``fresh_block_write`` the step writes a single token (the position
     after sequence 0's context) into the next free block instead of one token
-    per sequence at position n-1.
+    per sequence at position n-1. ``shuffle_pool=False`` hands out blocks in
+    ascending order, so each request's blocks are contiguous in the pool (the
+    permutation is still drawn, so every value matches the shuffled layout).
     """
     if rng is None:
         rng = np.random.default_rng(seed)
@@ -212,6 +215,8 @@ def make_paged_batch(*, num_q_heads: int, num_kv_heads: int, head_dim: int, dtyp
         raise ValueError("pool smaller than the blocks the batch needs")
 
     order = rng.permutation(num_blocks)
+    if not shuffle_pool:
+        order = np.arange(num_blocks)
     pool = BlockPool(num_blocks, order)
     tables: list[RequestTable] = []
     for s in range(num_seqs):

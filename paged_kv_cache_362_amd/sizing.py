@@ -86,3 +86,12 @@ def reshape_and_cache_bytes(num_tokens: int, num_kv_heads: int, head_dim: int,
 def decode_flops(context_lens: Sequence[int], num_q_heads: int, head_dim: int) -> int:
     """Multiply-adds of QK^T and PV, two flops each."""
     return 4 * sum(int(n) for n in context_lens) * num_q_heads * head_dim
+
+
+def internal_fragmentation(context_lens: Sequence[int], block_size: int) -> float:
+    """Share of allocated slots that hold no token: each sequence owns
+    ceil(n / B) blocks and uses n of their slots ([KVP] "Block 大小的选择":
+    larger blocks mean fewer table entries but more waste in the last block)."""
+    used = sum(int(n) for n in context_lens)
+    allocated = sum(blocks_needed(int(n), block_size) * block_size for n in context_lens)
+    return 0.0 if allocated == 0 else (allocated - used) / allocated

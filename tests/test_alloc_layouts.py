@@ -136,3 +136,15 @@ def test_bf16_rounding_is_nearest_even():
     back = O.to_f64(bits, "bf16")
     assert back[0] == 1.0 and back[1] == 1.0 and back[2] == 1.0 + 2 ** -6
     assert np.isnan(back[4])
+
+
+def test_contiguous_pool_keeps_values_and_orders_blocks():
+    a = layouts.make_paged_batch(num_q_heads=2, num_kv_heads=2, head_dim=64, dtype="f16",
+                                 block_size=16, context_lens=np.array([40, 70]), seed=9)
+    b = layouts.make_paged_batch(num_q_heads=2, num_kv_heads=2, head_dim=64, dtype="f16",
+                                 block_size=16, context_lens=np.array([40, 70]), seed=9,
+                                 shuffle_pool=False)
+    assert np.array_equal(a.q, b.q) and np.array_equal(a.k_cache, b.k_cache)
+    # blocks handed out in ascending order: sequence 0 gets 0..2, sequence 1 gets 3..7
+    assert list(b.block_tables[0, :3]) == [0, 1, 2]
+    assert list(b.block_tables[1, :5]) == [3, 4, 5, 6, 7]

@@ -83,3 +83,11 @@ def test_decode_bytes_formula():
     assert b == 50 * 4 * 64 * 2 * 4 + 2 * 4 * 64 * 4 + 4 * 4 + 4
     shared = sizing.decode_algorithmic_bytes([64, 64], 2, 2, 8, 2, 32, unique_blocks=3)
     assert shared == 3 * 32 * 2 * 8 * 2 * 2 + 2 * 2 * 2 * 8 * 2 + 4 * 4 + 8
+
+
+def test_internal_fragmentation():
+    # 50 tokens in 16-token blocks: 64 slots, 14 empty ([INFRA] §3.3 example)
+    assert sizing.internal_fragmentation([50], 16) == 14 / 64
+    assert sizing.internal_fragmentation([64, 32], 32) == 0.0
+    assert sizing.internal_fragmentation([1], 8) == 7 / 8
+    assert sizing.internal_fragmentation([], 16) == 0.0
