@@ -60,6 +60,9 @@ def parse_args(argv=None):
     ap.add_argument("--paging-sweep", action="store_true",
                     help="decode on contiguous vs shuffled block tables at block sizes "
                          "8/16/32/64 (LLaMA-7B-layer shapes); prints one JSON line")
+    ap.add_argument("--block-ops", action="store_true",
+                    help="copy-on-write and swap block copies at LLaMA-7B-layer block shapes "
+                         "beside plain contiguous copies of the same bytes; one JSON line")
     return ap.parse_args(argv)
 
 
@@ -163,6 +166,62 @@ def paging_sweep(args) -> dict:
             "steps": args.steps, "warmup": args.warmup, "statistic": "median"}
 
 
+def block_ops(args) -> dict:
+    """Whole-block copies ([INFRA] §4.3): copy-on-write inside the device pool
+    and swapping between the device pool and a pinned host pool, each against a
+    plain contiguous copy of the same bytes (torch copy_: a device kernel, or
+    the DMA engines across the host link), the rate those copies can reach."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_362_amd import ops
+
+    dev = torch.device("cuda:0")
+    hkv, bs, d, n_dev, n_host, pairs = 32, 16, 128, 4096, 1024, 512
+    rng = np.random.default_rng(5)
+    kc = torch.randn(n_dev, hkv, bs, d, dtype=torch.float16, device=dev)
+    vc = torch.randn_like(kc)
+    hk = torch.zeros(n_host, hkv, bs, d, dtype=torch.float16, pin_memory=True)
+    hv = torch.zeros(n_host, hkv, bs, d, dtype=torch.float16, pin_memory=True)
+    perm = rng.permutation(n_dev)
+    m = lambda a, b: torch.from_numpy(np.stack([a, b], 1).astype(np.int32)).to(dev)  # noqa: E731
+    cow = m(perm[:pairs], perm[pairs:2 * pairs])
+    out_map = m(perm[:pairs], rng.permutation(n_host)[:pairs])
+    in_map = m(out_map[:, 1].cpu().numpy(), perm[2 * pairs:3 * pairs])
+    moved = 2 * pairs * kc[0].numel() * kc.element_size()       # K and V bytes per call
+    flat_dev = kc[:2 * pairs].view(-1)
+    flat_dst = vc[2 * pairs:4 * pairs].view(-1)
+    flat_host = torch.empty(flat_dev.numel(), dtype=torch.float16, pin_memory=True)
+    cases = {
+        "copy_blocks (device, copy-on-write)": lambda: ops.copy_blocks(kc, vc, cow),
+        "contiguous device copy_": lambda: flat_dst.copy_(flat_dev),
+        "swap_blocks out (device -> pinned host)": lambda: ops.swap_blocks(kc, vc, hk, hv,
+                                                                            out_map),
+        "contiguous D2H copy_ (DMA)": lambda: flat_host.copy_(flat_dev, non_blocking=True),
+        "swap_blocks in (pinned host -> device)": lambda: ops.swap_blocks(hk, hv, kc, vc,
+                                                                           in_map),
+        "contiguous H2D copy_ (DMA)": lambda: flat_dev.copy_(flat_host, non_blocking=True),
+    }
+    rows = []
+    for name, fn in cases.items():
+        for _ in range(args.warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+        rows.append({"op": name, "us": round(ms * 1e3, 1),
+                     "GBps_moved": round(moved / ms / 1e6, 1)})
+    return {"block_ops": rows, "pairs": pairs, "bytes_moved_per_call": moved,
+            "block": f"K and V, {hkv} KV heads x {bs} slots x D {d}, fp16 "
+                     f"({kc[0].numel() * 2 // 1024} KiB each)",
+            "note": "device copies read and write the bytes moved (HBM traffic twice that)",
+            "steps": args.steps, "warmup": args.warmup, "statistic": "median"}
+
+
 def cpu_baseline(batch, seconds: float) -> dict:
     """The float64 oracle on a bounded sample of the same batch, one thread."""
     import numpy as np
@@ -212,6 +271,9 @@ def main(argv=None) -> int:
         return 0
     if args.paging_sweep:
         print(json.dumps(paging_sweep(args)), flush=True)
+        return 0
+    if args.block_ops:
+        print(json.dumps(block_ops(args)), flush=True)
         return 0
 
     from paged_kv_cache_362_amd import layouts, ops, sizing

@@ -76,7 +76,8 @@ enum {
   PA_ERR_UNSUPPORTED = 3,        /* head_dim, block_size, dtype or group not built */
   PA_ERR_WORKSPACE_TOO_SMALL = 4,
   PA_ERR_HIP = 5,                /* the HIP runtime reported an error */
-  PA_ERR_BAD_INDEX = 6           /* PA_DEBUG: a device-side precondition failed */
+  PA_ERR_BAD_INDEX = 6,          /* PA_DEBUG: a device-side precondition failed */
+  PA_ERR_BAD_POINTER = 7         /* memory the GPU cannot address (e.g. pageable host) */
 };
 
 /* Element types of q, out, key, value and the pools (all the same). */
@@ -193,6 +194,49 @@ int32_t pa_decode_step(void *out, const void *q, const void *key,
                        int32_t max_blocks_per_seq, int32_t max_context_len,
                        int32_t dtype, void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/*
+ * pa_copy_blocks - copy whole physical blocks inside the pools
+ * (copy-on-write: several tables may point at one block, and a request about
+ * to write into a shared block first takes a private copy of it, [INFRA] §4.3).
+ *
+ * block_mapping int32 [num_pairs, 2]: pair i makes block block_mapping[2i+1]
+ * an exact copy of block block_mapping[2i], in k_cache and in v_cache (every
+ * KV head, every slot: num_kv_heads * block_size * head_dim elements each).
+ * Destinations must be distinct and must not be sources in the same call
+ * (checked under PA_DEBUG only); a pair naming a block outside [0, num_blocks)
+ * copies nothing. Supported shapes as for pa_reshape_and_cache. num_pairs may
+ * be 0 (no launch).
+ */
+int32_t pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_mapping,
+                       int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t dtype,
+                       void *stream);
+
+/*
+ * pa_swap_blocks - copy whole blocks from one pair of pools to another, for
+ * swapping: a preempted request's blocks move out to host memory and come back
+ * when it resumes, the table being the only thing that changes ([INFRA] §4.3).
+ *
+ * Pair i of block_mapping int32 [num_pairs, 2] (device memory) copies block
+ * block_mapping[2i] of (src_k, src_v) to block block_mapping[2i+1] of
+ * (dst_k, dst_v), every KV head and slot, bit for bit. Either pool pair may be
+ * pinned host memory the GPU can address (hipHostMalloc, e.g. torch's
+ * pin_memory=True); the kernel then reads or writes it over the host link.
+ * Each pool pointer is looked up with hipPointerGetAttributes (a few
+ * microseconds of host time per call): host pointers are translated to their
+ * device addresses, and memory that is neither device memory nor registered
+ * host memory gives PA_ERR_BAD_POINTER before anything is launched.
+ * src pools are [src_num_blocks, ...], dst pools [dst_num_blocks, ...]; the
+ * two pairs must not overlap. Destinations must be distinct and in range
+ * (checked under PA_DEBUG only); a pair outside either pool copies nothing.
+ * block_mapping may be device memory or pinned host memory.
+ */
+int32_t pa_swap_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_v,
+                       const int32_t *block_mapping, int32_t num_pairs,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t src_num_blocks, int32_t dst_num_blocks,
+                       int32_t dtype, void *stream);
 
 /* A static, human-readable name of a status code. */
 const char *pa_status_str(int32_t status);

@@ -31,6 +31,8 @@ What is computed, and where the pages fix it:
 * Cache write ([INFRA] §1.2, the cache append; §3.3, a new token going into the
   next slot of the request's last block): the new token's K and V rows are
   copied, unchanged, into the slot that names them.
+* Block copy ([INFRA] §4.3, copy-on-write of blocks that several tables share):
+  a whole physical block, every head and slot, copied unchanged.
 
 Readings taken where the pages are silent or inconsistent:
 
@@ -273,6 +275,36 @@ def ref_reshape_and_cache(key: np.ndarray, value: np.ndarray, k_cache: np.ndarra
     return k_new, v_new
 
 
+def ref_copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, block_mapping: np.ndarray):
+    """Copy whole physical blocks (every KV head, every slot), K and V.
+
+    block_mapping [P, 2] int: row (src, dst) makes block dst a copy of block
+    src, the step a copy-on-write takes before a shared block is written
+    ([INFRA] §4.3). Destinations are distinct and are not sources. Returns new
+    arrays; the inputs are not modified. Bit-exact by construction.
+    """
+    k_new = k_cache.copy()
+    v_new = v_cache.copy()
+    for src, dst in np.asarray(block_mapping).reshape(-1, 2):
+        k_new[int(dst)] = k_cache[int(src)]
+        v_new[int(dst)] = v_cache[int(src)]
+    return k_new, v_new
+
+
+def ref_swap_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray,
+                    dst_v: np.ndarray, block_mapping: np.ndarray):
+    """Copy whole blocks from one pair of pools to another (swap out to host
+    memory or back in, [INFRA] §4.3). Row (src, dst) of block_mapping makes
+    block dst of the destination pools a copy of block src of the source
+    pools. Returns new destination arrays; the inputs are not modified."""
+    k_new = dst_k.copy()
+    v_new = dst_v.copy()
+    for src, dst in np.asarray(block_mapping).reshape(-1, 2):
+        k_new[int(dst)] = src_k[int(src)]
+        v_new[int(dst)] = src_v[int(src)]
+    return k_new, v_new
+
+
 # ---------------------------------------------------------------------------
 # small helpers used by the tests' pins
 # ---------------------------------------------------------------------------
@@ -309,6 +341,6 @@ __all__ = [
     "DTYPES", "to_f64", "logical_block_of", "offset_in_block", "slot_of",
     "slots_of_sequence", "kv_head_for", "gather_rows", "softmax", "attend",
     "scale_as_f64", "ref_decode", "ref_decode_blockloop",
-    "ref_reshape_and_cache", "num_blocks_for", "bf16_round", "ulp_bf16",
+    "ref_reshape_and_cache", "ref_copy_blocks", "ref_swap_blocks", "num_blocks_for", "bf16_round", "ulp_bf16",
     "nan_count",
 ]

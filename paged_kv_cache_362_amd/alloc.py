@@ -31,10 +31,12 @@ class BlockPool:
 
     ``order`` fixes the sequence in which free blocks are handed out (a seeded
     permutation scatters a request's blocks over the pool). Freed blocks go to
-    the back of the list.
+    the back of the list. A device pool and the host pool that requests are
+    swapped out to are two BlockPools.
     """
 
-    def __init__(self, num_blocks: int, order: Iterable[int] | None = None):
+    def __init__(self, num_blocks: int, order: Iterable[int] | None = None,
+                 block_size_hint: int | None = None):
         if num_blocks < 0:
             raise ValueError("num_blocks must be >= 0")
         self.num_blocks = int(num_blocks)
@@ -43,6 +45,9 @@ class BlockPool:
             raise ValueError("order must be a permutation of range(num_blocks)")
         self._free = deque(seq)
         self._refs = [0] * num_blocks
+        # Tokens per block, when known: tables refuse to move between pools
+        # whose blocks differ in size.
+        self.block_size_hint = block_size_hint
 
     @property
     def num_free(self) -> int:
@@ -126,3 +131,59 @@ class RequestTable:
             self.pool.free(b)
         self.blocks = []
         self.num_tokens = 0
+
+    def fork(self) -> "RequestTable":
+        """A second table over the same blocks (a beam, or a request reusing
+        this one's prompt): the table is copied, the KV data is not ([INFRA]
+        §4.3, beam search sharing)."""
+        other = RequestTable(self.pool, self.block_size)
+        other.blocks = [self.pool.share(b) for b in self.blocks]
+        other.num_tokens = self.num_tokens
+        return other
+
+    def append_cow(self) -> tuple[int, list[tuple[int, int]]]:
+        """Reserve the next position, copying the last block first if another
+        table shares it (copy-on-write, [INFRA] §4.3).
+
+        Returns (slot of the new position, [(src_block, dst_block)] copies the
+        device must make before anything is written to that slot). A shared
+        block that is full is never written again, so only a partly filled
+        shared last block is copied.
+        """
+        pos = self.num_tokens
+        copies: list[tuple[int, int]] = []
+        if pos < len(self.blocks) * self.block_size:
+            last = self.blocks[-1]
+            if self.pool.refcount(last) > 1:
+                fresh = self.pool.alloc()
+                copies.append((last, fresh))
+                self.pool.free(last)
+                self.blocks[-1] = fresh
+        else:
+            self.blocks.append(self.pool.alloc())
+        self.num_tokens += 1
+        return self.slot(pos), copies
+
+    def move_to(self, target: BlockPool) -> list[tuple[int, int]]:
+        """Swap this request out to ``target`` (a host pool), or back in (a
+        device pool): every block gets a fresh block in ``target``, the old
+        ones are released, and the table now points into ``target``
+        ([INFRA] §4.3, preemption by swapping).
+
+        Returns [(old_block, new_block)] copies the device must make before the
+        old blocks are reused. Shared blocks are copied like the rest: the
+        moved request keeps a private copy and the other users keep theirs.
+        Raises PoolExhausted, changing nothing, if ``target`` is too small.
+        """
+        if target is self.pool:
+            raise ValueError("the table already lives in that pool")
+        if target.block_size_hint is not None and target.block_size_hint != self.block_size:
+            raise ValueError("the pools hold blocks of different sizes")
+        if target.num_free < len(self.blocks):
+            raise PoolExhausted(f"{len(self.blocks)} blocks needed, {target.num_free} free")
+        mapping = [(b, target.alloc()) for b in self.blocks]
+        for b in self.blocks:
+            self.pool.free(b)
+        self.pool = target
+        self.blocks = [new for _, new in mapping]
+        return mapping

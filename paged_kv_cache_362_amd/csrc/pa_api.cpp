@@ -18,7 +18,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 constexpr size_t kAlign = 256;
 
 bool debug_checks() {
@@ -117,6 +117,31 @@ WsLayout workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_
   return w;
 }
 
+// The address a kernel uses for p: p itself for device (or managed) memory,
+// the mapped device address for pinned host memory. Pageable host memory and
+// unknown pointers are refused: a kernel touching them would fault.
+int32_t device_address(const void *p, const void **dev) {
+  hipPointerAttribute_t a{};
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();  // do not leave the error for the next call
+    return PA_ERR_BAD_POINTER;
+  }
+  if (a.type == hipMemoryTypeDevice || a.isManaged) {
+    *dev = p;
+    return PA_OK;
+  }
+  if (a.type == hipMemoryTypeHost) {
+    void *d = nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void *>(p), 0) != hipSuccess || d == nullptr) {
+      (void)hipGetLastError();
+      return PA_ERR_BAD_POINTER;
+    }
+    *dev = d;
+    return PA_OK;
+  }
+  return PA_ERR_BAD_POINTER;
+}
+
 int32_t sync_copy_to_host(void *dst, const void *src, size_t bytes, hipStream_t stream) {
   if (bytes == 0) return PA_OK;
   if (hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, stream) != hipSuccess)
@@ -180,6 +205,7 @@ const char *pa_status_str(int32_t status) {
     case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case PA_ERR_HIP: return "HIP runtime error";
     case PA_ERR_BAD_INDEX: return "device-side index precondition violated (PA_DEBUG)";
+    case PA_ERR_BAD_POINTER: return "memory is neither GPU memory nor pinned host memory";
   }
   return "unknown status";
 }
@@ -221,6 +247,88 @@ int32_t pa_reshape_and_cache(const void *key, const void *value, void *k_cache, 
   p.block_shift = exact_log2(block_size);
   p.num_slots = num_slots;
   return pa::launch_reshape_and_cache(p, s) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int32_t pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_mapping,
+                       int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t dtype, void *stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks < 0) return PA_ERR_BAD_SHAPE;
+  if (elem_bytes(dtype) == 0 || !head_dim_ok(head_dim) || !block_size_ok(block_size))
+    return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_mapping) return PA_ERR_NULL_POINTER;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_UNSUPPORTED;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    std::vector<int32_t> map(size_t(num_pairs) * 2);
+    int32_t st = sync_copy_to_host(map.data(), block_mapping, sizeof(int32_t) * map.size(), s);
+    if (st != PA_OK) return st;
+    std::unordered_set<int32_t> dsts, srcs;
+    for (int32_t i = 0; i < num_pairs; ++i) {
+      const int32_t a = map[2 * i], b = map[2 * i + 1];
+      if (a < 0 || a >= num_blocks || b < 0 || b >= num_blocks) return PA_ERR_BAD_INDEX;
+      if (!dsts.insert(b).second) return PA_ERR_BAD_INDEX;
+      srcs.insert(a);
+    }
+    for (int32_t b : dsts)
+      if (srcs.count(b)) return PA_ERR_BAD_INDEX;  // a destination that is also a source
+  }
+  pa::BlockCopyParams p{};
+  p.src_k = k_cache;
+  p.src_v = v_cache;
+  p.dst_k = k_cache;
+  p.dst_v = v_cache;
+  p.block_mapping = block_mapping;
+  p.num_pairs = num_pairs;
+  p.src_blocks = num_blocks;
+  p.dst_blocks = num_blocks;
+  p.block_bytes = int64_t(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
+  return pa::launch_copy_blocks(p, s) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int32_t pa_swap_blocks(const void *src_k, const void *src_v, void *dst_k, void *dst_v,
+                       const int32_t *block_mapping, int32_t num_pairs, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t src_num_blocks,
+                       int32_t dst_num_blocks, int32_t dtype, void *stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || src_num_blocks < 0 || dst_num_blocks < 0)
+    return PA_ERR_BAD_SHAPE;
+  if (elem_bytes(dtype) == 0 || !head_dim_ok(head_dim) || !block_size_ok(block_size))
+    return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !block_mapping) return PA_ERR_NULL_POINTER;
+  if (!aligned16(src_k) || !aligned16(src_v) || !aligned16(dst_k) || !aligned16(dst_v))
+    return PA_ERR_UNSUPPORTED;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const void *dev[4];
+  const void *host[4] = {src_k, src_v, dst_k, dst_v};
+  for (int i = 0; i < 4; ++i) {
+    const int32_t st = device_address(host[i], &dev[i]);
+    if (st != PA_OK) return st;
+  }
+  const void *map_dev = nullptr;
+  if (const int32_t st = device_address(block_mapping, &map_dev); st != PA_OK) return st;
+  if (debug_checks()) {
+    std::vector<int32_t> map(size_t(num_pairs) * 2);
+    int32_t st = sync_copy_to_host(map.data(), block_mapping, sizeof(int32_t) * map.size(), s);
+    if (st != PA_OK) return st;
+    std::unordered_set<int32_t> dsts;
+    for (int32_t i = 0; i < num_pairs; ++i) {
+      const int32_t a = map[2 * i], b = map[2 * i + 1];
+      if (a < 0 || a >= src_num_blocks || b < 0 || b >= dst_num_blocks) return PA_ERR_BAD_INDEX;
+      if (!dsts.insert(b).second) return PA_ERR_BAD_INDEX;
+    }
+  }
+  pa::BlockCopyParams p{};
+  p.src_k = dev[0];
+  p.src_v = dev[1];
+  p.dst_k = const_cast<void *>(dev[2]);
+  p.dst_v = const_cast<void *>(dev[3]);
+  p.block_mapping = static_cast<const int32_t *>(map_dev);
+  p.num_pairs = num_pairs;
+  p.src_blocks = src_num_blocks;
+  p.dst_blocks = dst_num_blocks;
+  p.block_bytes = int64_t(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
+  return pa::launch_copy_blocks(p, s) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

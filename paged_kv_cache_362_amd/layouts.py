@@ -315,6 +315,17 @@ def scaled_config(config: int, seed: int | None = None, poison: bool = False,
         name=f"config{config} scaled", **kw)
 
 
+def to_torch(a: np.ndarray, dtype: str):
+    """A host array in storage form as a CPU torch tensor (bf16 bit patterns
+    become bfloat16)."""
+    import torch
+
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    return torch.from_numpy(a)
+
+
 def to_device(batch: PagedBatch, device="cuda"):
     """torch tensors of a batch on ``device`` (bf16 bit patterns become bfloat16)."""
     import torch

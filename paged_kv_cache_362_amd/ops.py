@@ -17,7 +17,8 @@ DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 PA_OK = 0
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_BAD_SHAPE", 3: "PA_ERR_UNSUPPORTED",
-          4: "PA_ERR_WORKSPACE_TOO_SMALL", 5: "PA_ERR_HIP", 6: "PA_ERR_BAD_INDEX"}
+          4: "PA_ERR_WORKSPACE_TOO_SMALL", 5: "PA_ERR_HIP", 6: "PA_ERR_BAD_INDEX",
+          7: "PA_ERR_BAD_POINTER"}
 
 
 class PagedAttentionError(RuntimeError):
@@ -42,6 +43,11 @@ def _stream(t: torch.Tensor) -> ctypes.c_void_p:
 def _require(cond: bool, msg: str) -> None:
     if not cond:
         raise ValueError(msg)
+
+
+def _addressable(t: torch.Tensor) -> bool:
+    """On the GPU, or pinned host memory the GPU can read and write."""
+    return t.is_cuda or t.is_pinned()
 
 
 def _on_gpu(*ts: torch.Tensor) -> None:
@@ -175,3 +181,43 @@ def decode_step(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
         workspace.numel() * workspace.element_size(), _stream(q))
     _check("pa_decode_step", code)
     return out
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor,
+                block_mapping: torch.Tensor) -> None:
+    """Copy-on-write: for each row (src, dst) of block_mapping int32 [P, 2],
+    block dst of both pools becomes a copy of block src."""
+    _on_gpu(k_cache, v_cache, block_mapping)
+    _require(k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "pools must be [N, Hkv, B, D]")
+    _require(k_cache.dtype == v_cache.dtype, "one dtype for both pools")
+    _require(block_mapping.dtype == torch.int32 and block_mapping.dim() == 2 and
+             block_mapping.shape[1] == 2, "block_mapping must be int32 [P, 2]")
+    n, hkv, bs, d = k_cache.shape
+    code = lib().pa_copy_blocks(_dev_ptr(k_cache), _dev_ptr(v_cache), _dev_ptr(block_mapping),
+                                block_mapping.shape[0], hkv, d, bs, n,
+                                dtype_code(k_cache.dtype), _stream(k_cache))
+    _check("pa_copy_blocks", code)
+
+
+def swap_blocks(src_k: torch.Tensor, src_v: torch.Tensor, dst_k: torch.Tensor,
+                dst_v: torch.Tensor, block_mapping: torch.Tensor) -> None:
+    """Swap-out / swap-in: for each row (src, dst) of block_mapping int32 [P, 2]
+    (on the GPU), block dst of (dst_k, dst_v) becomes a copy of block src of
+    (src_k, src_v). Pools may live on the GPU or in pinned host memory; the
+    copy runs on the current stream of the GPU holding block_mapping."""
+    for t in (src_k, src_v, dst_k, dst_v):
+        _require(_addressable(t), "pools must be on the GPU or in pinned host memory")
+        _require(t.is_contiguous(), "pools must be contiguous")
+    _require(block_mapping.is_cuda and block_mapping.dtype == torch.int32 and
+             block_mapping.dim() == 2 and block_mapping.shape[1] == 2 and
+             block_mapping.is_contiguous(), "block_mapping must be int32 [P, 2] on the GPU")
+    _require(src_k.shape == src_v.shape and dst_k.shape == dst_v.shape and
+             src_k.shape[1:] == dst_k.shape[1:] and src_k.dim() == 4,
+             "pools must be [N, Hkv, B, D] with matching block shapes")
+    _require(src_k.dtype == src_v.dtype == dst_k.dtype == dst_v.dtype, "one dtype")
+    _, hkv, bs, d = src_k.shape
+    code = lib().pa_swap_blocks(_dev_ptr(src_k), _dev_ptr(src_v), _dev_ptr(dst_k),
+                                _dev_ptr(dst_v), _dev_ptr(block_mapping),
+                                block_mapping.shape[0], hkv, d, bs, src_k.shape[0],
+                                dst_k.shape[0], dtype_code(src_k.dtype), _stream(block_mapping))
+    _check("pa_swap_blocks", code)

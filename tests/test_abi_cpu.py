@@ -33,7 +33,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("pa_reshape_and_cache", "pa_decode", "pa_decode_step", "pa_decode_workspace_size",
-              "pa_status_str", "pa_abi_version"):
+              "pa_copy_blocks", "pa_swap_blocks", "pa_status_str", "pa_abi_version"):
         assert n in names
 
 
@@ -44,8 +44,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.pa_abi_version() == 2
-    for code in range(7):
+    assert lib.pa_abi_version() == 3
+    for code in range(8):
         assert lib.pa_status_str(code)
     assert lib.pa_status_str(99) == b"unknown status"
 
@@ -141,3 +141,27 @@ def test_decode_step_rejects_bad_arguments_before_launch(lib):
     assert call(maxlen=65) == SHAPE
     assert call(ws=16, wsb=100) == WS
     assert call(S=0, q=None, out=None, slots=None) == OK
+
+
+def test_copy_blocks_rejects_bad_arguments_before_launch(lib):
+    f = lib.pa_copy_blocks
+    assert f(16, 16, None, 1, 4, 64, 16, 8, F16, None) == NULLP
+    assert f(16, 16, 16, -1, 4, 64, 16, 8, F16, None) == SHAPE
+    assert f(16, 16, 16, 1, 4, 80, 16, 8, F16, None) == UNSUP
+    assert f(16, 16, 16, 1, 4, 64, 12, 8, F16, None) == UNSUP
+    assert f(24, 16, 16, 1, 4, 64, 16, 8, F16, None) == UNSUP  # misaligned
+    assert f(None, None, None, 0, 4, 64, 16, 8, F16, None) == OK  # nothing to copy
+
+
+def test_swap_blocks_rejects_bad_arguments_before_launch(lib):
+    f = lib.pa_swap_blocks
+    assert f(16, 16, 16, 16, None, 1, 4, 64, 16, 8, 8, F16, None) == NULLP
+    assert f(16, None, 16, 16, 16, 1, 4, 64, 16, 8, 8, F16, None) == NULLP
+    assert f(16, 16, 16, 16, 16, -1, 4, 64, 16, 8, 8, F16, None) == SHAPE
+    assert f(16, 16, 16, 16, 16, 1, 4, 64, 16, -1, 8, F16, None) == SHAPE
+    assert f(16, 16, 16, 16, 16, 1, 0, 64, 16, 8, 8, F16, None) == SHAPE
+    assert f(16, 16, 16, 16, 16, 1, 4, 80, 16, 8, 8, F16, None) == UNSUP
+    assert f(16, 16, 16, 16, 16, 1, 4, 64, 12, 8, 8, F16, None) == UNSUP
+    assert f(16, 16, 16, 16, 16, 1, 4, 64, 16, 8, 8, 7, None) == UNSUP
+    assert f(16, 16, 24, 16, 16, 1, 4, 64, 16, 8, 8, F16, None) == UNSUP  # misaligned
+    assert f(None, None, None, None, None, 0, 4, 64, 16, 8, 8, F16, None) == OK

@@ -148,3 +148,68 @@ def test_contiguous_pool_keeps_values_and_orders_blocks():
     # blocks handed out in ascending order: sequence 0 gets 0..2, sequence 1 gets 3..7
     assert list(b.block_tables[0, :3]) == [0, 1, 2]
     assert list(b.block_tables[1, :5]) == [3, 4, 5, 6, 7]
+
+
+def test_fork_shares_blocks_and_copy_on_write():
+    """[INFRA] §4.3: a beam copies the table, not the KV; writing into a shared,
+    partly filled block first copies it."""
+    pool = BlockPool(16, range(16))
+    a = RequestTable(pool, 16)
+    a.append_tokens(40)                      # blocks 0, 1, 2 (2 is half full)
+    b = a.fork()
+    assert b.blocks == a.blocks == [0, 1, 2]
+    assert [pool.refcount(x) for x in (0, 1, 2)] == [2, 2, 2]
+    slot, copies = b.append_cow()            # position 40 is in shared block 2
+    assert copies == [(2, 3)] and b.blocks == [0, 1, 3] and slot == 3 * 16 + 8
+    assert pool.refcount(2) == 1 and pool.refcount(3) == 1
+    slot, copies = a.append_cow()            # block 2 is now a's alone
+    assert copies == [] and slot == 2 * 16 + 8
+    b.append_tokens(7)                       # fills block 3 to 48 tokens
+    slot, copies = b.append_cow()            # position 48 needs a new block
+    assert copies == [] and b.blocks[-1] == 4 and slot == 4 * 16
+    b.release()
+    assert [pool.refcount(x) for x in (0, 1, 3, 4)] == [1, 1, 0, 0]
+    a.release()
+    assert pool.num_free == 16
+
+
+def test_full_shared_block_is_never_copied():
+    pool = BlockPool(8, range(8))
+    a = RequestTable(pool, 16)
+    a.append_tokens(32)                      # blocks 0, 1, both full
+    b = a.fork()
+    slot, copies = b.append_cow()
+    assert copies == [] and b.blocks == [0, 1, 2] and slot == 32
+
+
+def test_swap_out_and_in_moves_the_table():
+    """[INFRA] §4.3: preemption moves a request's blocks to a host pool and
+    back; the copies to make are returned, the old blocks are released."""
+    dev = BlockPool(8, range(8), block_size_hint=16)
+    host = BlockPool(4, range(4), block_size_hint=16)
+    a = RequestTable(dev, 16)
+    a.append_tokens(40)                      # device blocks 0, 1, 2
+    b = a.fork()                             # shares them
+    out = a.move_to(host)
+    assert out == [(0, 0), (1, 1), (2, 2)] and a.pool is host and a.blocks == [0, 1, 2]
+    assert [dev.refcount(x) for x in (0, 1, 2)] == [1, 1, 1]   # b keeps them
+    assert a.slot(39) == 2 * 16 + 7 and a.num_tokens == 40
+    b.release()
+    dev.alloc()                              # block 3 taken meanwhile
+    back = a.move_to(dev)
+    assert back == [(0, 4), (1, 5), (2, 6)] and a.blocks == [4, 5, 6]
+    assert host.num_free == 4 and dev.num_free == 8 - 4
+    with pytest.raises(ValueError):
+        a.move_to(dev)
+
+
+def test_swap_needs_room_and_equal_blocks():
+    dev = BlockPool(8, range(8), block_size_hint=16)
+    a = RequestTable(dev, 16)
+    a.append_tokens(40)
+    small = BlockPool(2, range(2), block_size_hint=16)
+    with pytest.raises(PoolExhausted):
+        a.move_to(small)
+    assert a.pool is dev and a.blocks == [0, 1, 2] and small.num_free == 2
+    with pytest.raises(ValueError):
+        a.move_to(BlockPool(8, range(8), block_size_hint=32))

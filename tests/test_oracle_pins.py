@@ -404,3 +404,50 @@ def test_planted_mistakes_are_caught(mutant, monkeypatch):
         except Exception:  # AssertionError or an index error the mistake causes
             caught.append(pin.__name__)
     assert caught, f"no pin catches the planted mistake {mutant}"
+
+
+def test_copy_blocks_oracle():
+    """Block copy: destination blocks equal their sources byte for byte, every
+    other block is untouched, the inputs are not modified."""
+    rng = np.random.default_rng(12)
+    kc = rng.standard_normal((6, 2, 4, 8)).astype(np.float16)
+    vc = rng.standard_normal((6, 2, 4, 8)).astype(np.float16)
+    k2, v2 = O.ref_copy_blocks(kc, vc, np.array([[1, 4], [0, 5]]))
+    assert np.array_equal(k2[4].view(np.int16), kc[1].view(np.int16))
+    assert np.array_equal(v2[5].view(np.int16), vc[0].view(np.int16))
+    for b in (0, 1, 2, 3):
+        assert np.array_equal(k2[b].view(np.int16), kc[b].view(np.int16))
+    assert not np.array_equal(k2[4], kc[4])
+
+
+def test_swap_out_and_back_in_preserves_attention():
+    """[INFRA] §4.3: a preempted request's blocks go to host memory and come
+    back, usually to other device blocks; only its table changes. Attention
+    over the moved-back blocks through the new table equals attention before
+    the swap, exactly, and the host pool holds the blocks bit for bit."""
+    b = layouts.scaled_config(2, max_seqs=3, max_len=200)
+    base = O.ref_decode(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens,
+                        b.scale, b.dtype)
+    rng = np.random.default_rng(19)
+    used = sorted({int(x) for row, n in zip(b.block_tables, b.context_lens)
+                   for x in row[:O.num_blocks_for(int(n), b.block_size)]})
+    host_k = np.zeros((len(used) + 3,) + b.k_cache.shape[1:], b.k_cache.dtype)
+    host_v = np.zeros_like(host_k)
+    host_of = dict(zip(used, rng.permutation(len(host_k))[:len(used)]))
+    out_map = np.array(sorted(host_of.items()), np.int32)
+    host_k, host_v = O.ref_swap_blocks(b.k_cache, b.v_cache, host_k, host_v, out_map)
+    for dev, host in host_of.items():
+        assert np.array_equal(host_k[host].view(np.uint8), b.k_cache[dev].view(np.uint8))
+        assert np.array_equal(host_v[host].view(np.uint8), b.v_cache[dev].view(np.uint8))
+    # back in, to a different device placement, over a cleared device pool
+    back_of = dict(zip(used, rng.permutation(b.num_blocks)[:len(used)]))
+    in_map = np.array([(host_of[u], back_of[u]) for u in used], np.int32)
+    dev_k = np.full_like(b.k_cache, np.nan)
+    dev_v = np.full_like(b.v_cache, np.nan)
+    dev_k, dev_v = O.ref_swap_blocks(host_k, host_v, dev_k, dev_v, in_map)
+    bt = b.block_tables.copy()
+    for i, n in enumerate(b.context_lens):
+        nb = O.num_blocks_for(int(n), b.block_size)
+        bt[i, :nb] = [back_of[int(x)] for x in b.block_tables[i, :nb]]
+    moved = O.ref_decode(b.q, dev_k, dev_v, bt, b.context_lens, b.scale, b.dtype)
+    assert np.array_equal(base, moved)
