@@ -13,6 +13,7 @@
 #include <unordered_set>
 #include <vector>
 
+#include "pa_blocks.h"
 #include "pa_internal.h"
 #include "pagedattn.h"
 

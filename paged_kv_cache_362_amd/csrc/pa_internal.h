@@ -64,28 +64,12 @@ struct CacheParams {
   int64_t num_slots;  // num_blocks * block_size
 };
 
-// Whole-block copies from (src_k, src_v) to (dst_k, dst_v): pair i of
-// block_mapping [num_pairs, 2] copies block block_mapping[2i] of the source
-// pools to block block_mapping[2i + 1] of the destination pools.
-struct BlockCopyParams {
-  const void *src_k;
-  const void *src_v;
-  void *dst_k;
-  void *dst_v;
-  const int32_t *block_mapping;
-  int num_pairs;
-  int src_blocks;       // blocks in the source pools
-  int dst_blocks;       // blocks in the destination pools
-  int64_t block_bytes;  // num_kv_heads * block_size * head_dim * element bytes
-};
-
 // kStageFlat: balanced single launch. kStageBoth: fixed partitions, then the
 // reduce. kStagePartitions / kStageReduce: one of those two launches.
 enum DecodeStage { kStageBoth = 0, kStagePartitions = 1, kStageReduce = 2, kStageFlat = 3 };
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream, DecodeStage stage);
 hipError_t launch_reshape_and_cache(const CacheParams &p, hipStream_t stream);
-hipError_t launch_copy_blocks(const BlockCopyParams &p, hipStream_t stream);
 
 // Dynamic LDS of the balanced form's plan: tile prefix sums [S + 1], clamped
 // lengths [S] and this step's slots [S].
