@@ -33,6 +33,11 @@ What is computed, and where the pages fix it:
   copied, unchanged, into the slot that names them.
 * Block copy ([INFRA] §4.3, copy-on-write of blocks that several tables share):
   a whole physical block, every head and slot, copied unchanged.
+* Multi-token (chunked-prefill) attention ([INFRA] §1.1 applied to every
+  token of a chunk; [OPS] calls the operator with a whole sequence of queries,
+  shape [1, 32, 8192, 64], and max_new_tokens = seq_len): each query token of
+  the chunk sees exactly what it would see had the tokens been decoded one at
+  a time, i.e. the cached keys up to and including its own position.
 
 Readings taken where the pages are silent or inconsistent:
 
@@ -49,6 +54,13 @@ Readings taken where the pages are silent or inconsistent:
   head_dim] ([OPS] keeps the K half and the V half of a page apart).
 * A slot is ``block_id * block_size + offset``; a negative slot means "write
   nothing" for that token.
+* A chunk of L query tokens of a sequence whose cache holds n tokens (the
+  chunk's own K/V already written) occupies positions n - L .. n - 1: the
+  chunk is the newest part of the context. Query token t (position
+  n - L + t) attends to positions 0 .. n - L + t (causal, the plain reading of
+  the per-step formula of [INFRA] §1.1 for a token at that step). Chunks of
+  all sequences are packed along one token axis, sequence s owning tokens
+  query_start_loc[s] .. query_start_loc[s+1] - 1.
 
 Storage dtypes: "f32" (numpy float32), "f16" (numpy float16) and "bf16"
 (numpy uint16 holding the bfloat16 bit pattern). Every value is widened to
@@ -207,6 +219,77 @@ def ref_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
     return out
 
 
+def query_position(context_len: int, chunk_len: int, t: int) -> int:
+    """Position in the sequence of token t of a chunk of chunk_len tokens that
+    ends the sequence's context_len cached tokens."""
+    return context_len - chunk_len + t
+
+
+def visible_keys(position: int) -> int:
+    """Number of cached positions a query at ``position`` attends to (causal:
+    every position up to and including its own)."""
+    return position + 1
+
+
+def ref_prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                block_tables: np.ndarray, context_lens: np.ndarray,
+                query_start_loc: np.ndarray, scale: float, dtype: str) -> np.ndarray:
+    """Multi-token (chunked-prefill) paged attention, float64.
+
+    q               [T, Hq, D] storage: the chunks of all sequences, packed
+    query_start_loc [S + 1] int: sequence s owns tokens qsl[s] .. qsl[s+1]-1
+    context_lens    [S] int: cached tokens of sequence s, chunk included
+                    (chunk length <= context length)
+    k_cache, v_cache, block_tables as for ``ref_decode``.
+
+    Returns out [T, Hq, D] float64: every query token attends, head by head,
+    to its sequence's cached rows up to and including its own position.
+    """
+    num_tokens, num_q_heads, head_dim = q.shape
+    num_kv_heads = k_cache.shape[1]
+    if num_q_heads % num_kv_heads:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    group = num_q_heads // num_kv_heads
+    qsl = [int(x) for x in query_start_loc]
+    if qsl[0] != 0 or qsl[-1] != num_tokens or any(b < a for a, b in zip(qsl, qsl[1:])):
+        raise ValueError("query_start_loc must rise from 0 to the number of tokens")
+    sc = scale_as_f64(scale)
+    q64 = to_f64(q, dtype)
+    out = np.zeros((num_tokens, num_q_heads, head_dim), dtype=np.float64)
+    for s in range(len(qsl) - 1):
+        n = int(context_lens[s])
+        chunk = qsl[s + 1] - qsl[s]
+        if chunk > n:
+            raise ValueError("a chunk cannot be longer than its sequence's context")
+        if chunk == 0:
+            continue
+        row = block_tables[s]
+        for kh in range(num_kv_heads):
+            keys = gather_rows(k_cache, row, n, kh, dtype)
+            vals = gather_rows(v_cache, row, n, kh, dtype)
+            for t in range(chunk):
+                seen = visible_keys(query_position(n, chunk, t))
+                for h in range(num_q_heads):
+                    if kv_head_for(h, group) != kh:
+                        continue
+                    _, o = attend(q64[qsl[s] + t, h], keys[:seen], vals[:seen], sc)
+                    out[qsl[s] + t, h] = o
+    return out
+
+
+def prefill_flops(context_lens, query_start_loc, num_q_heads: int, head_dim: int) -> int:
+    """Multiply-adds x 2 of the two products (scores and weighted values) a
+    causal chunked prefill must do: 4 * D per (query head, query token,
+    visible key)."""
+    total = 0
+    qsl = [int(x) for x in query_start_loc]
+    for s in range(len(qsl) - 1):
+        n, chunk = int(context_lens[s]), qsl[s + 1] - qsl[s]
+        seen = sum(visible_keys(query_position(n, chunk, t)) for t in range(chunk))
+        total += 4 * head_dim * num_q_heads * seen
+    return total
+
+
 def ref_decode_blockloop(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                          block_tables: np.ndarray, context_lens: np.ndarray,
                          scale: float, dtype: str) -> np.ndarray:
@@ -341,6 +424,7 @@ __all__ = [
     "DTYPES", "to_f64", "logical_block_of", "offset_in_block", "slot_of",
     "slots_of_sequence", "kv_head_for", "gather_rows", "softmax", "attend",
     "scale_as_f64", "ref_decode", "ref_decode_blockloop",
-    "ref_reshape_and_cache", "ref_copy_blocks", "ref_swap_blocks", "num_blocks_for", "bf16_round", "ulp_bf16",
+    "ref_reshape_and_cache", "ref_copy_blocks", "ref_swap_blocks", "ref_prefill",
+    "prefill_flops", "query_position", "visible_keys", "num_blocks_for", "bf16_round", "ulp_bf16",
     "nan_count",
 ]

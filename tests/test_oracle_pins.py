@@ -329,6 +329,93 @@ def pin_bf16_widening():
     assert list(O.bf16_round(x)) == [1.0, 1.0 + 2 ** -6, 1.0, -2.5]
 
 
+# --- multi-token (chunked-prefill) attention --------------------------------
+
+def _prefill_case(rng, hq, hkv, d, bs, lens, chunks):
+    """Random pools plus packed queries: sequence s has a chunk of chunks[s]
+    query tokens ending its lens[s] cached tokens."""
+    _, kc, vc, bt, cl, dk, dv = _random_case(rng, len(lens), hq, hkv, d, bs, lens)
+    qsl = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = rng.standard_normal((int(qsl[-1]), hq, d)).astype(np.float32)
+    return q, kc, vc, bt, cl, qsl, dk, dv
+
+
+def pin_prefill_matches_library_attention():
+    """A library routine: torch's scaled_dot_product_attention (CPU, float64)
+    over the contiguous rows, with an explicit causal mask offset so that the
+    chunk's queries sit at the end of the context."""
+    rng = np.random.default_rng(31)
+    for hq, hkv, d, bs, lens, chunks in [(4, 2, 8, 4, [13, 9], [5, 9]),
+                                         (2, 2, 16, 8, [40, 3, 17], [40, 1, 6]),
+                                         (6, 3, 4, 2, [11], [7])]:
+        q, kc, vc, bt, cl, qsl, dk, dv = _prefill_case(rng, hq, hkv, d, bs, lens, chunks)
+        scale = 1.0 / math.sqrt(d)
+        got = O.ref_prefill(q, kc, vc, bt, cl, qsl, scale, "f32")
+        g = hq // hkv
+        for s, (n, c) in enumerate(zip(lens, chunks)):
+            qs = torch.from_numpy(q[qsl[s]:qsl[s + 1]].astype(np.float64)).transpose(0, 1)
+            ks = torch.from_numpy(dk[s].astype(np.float64)).transpose(0, 1)
+            vs = torch.from_numpy(dv[s].astype(np.float64)).transpose(0, 1)
+            ks = ks.repeat_interleave(g, dim=0)
+            vs = vs.repeat_interleave(g, dim=0)
+            allowed = torch.arange(n)[None, :] <= (n - c + torch.arange(c))[:, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qs, ks, vs, attn_mask=allowed, scale=float(np.float32(scale)))
+            np.testing.assert_allclose(got[qsl[s]:qsl[s + 1]],
+                                       ref.transpose(0, 1).numpy(), rtol=0, atol=1e-12)
+
+
+def pin_prefill_single_token_chunks_are_decode():
+    """Special case: chunks of one token are decode steps."""
+    b = layouts.scaled_config(3, max_seqs=4, max_len=300)
+    qsl = np.arange(b.num_seqs + 1, dtype=np.int32)
+    got = O.ref_prefill(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, qsl,
+                        b.scale, b.dtype)
+    want = O.ref_decode(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, b.scale,
+                        b.dtype)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-13)
+
+
+def pin_prefill_first_token_is_its_value_row():
+    """Closed form: the first token of a whole-sequence prefill sees only
+    itself, so its output is its own V row, exactly."""
+    rng = np.random.default_rng(32)
+    q, kc, vc, bt, cl, qsl, dk, dv = _prefill_case(rng, 4, 4, 8, 4, [9, 6], [9, 6])
+    got = O.ref_prefill(q, kc, vc, bt, cl, qsl, 0.3, "f32")
+    for s in range(2):
+        for h in range(4):
+            assert np.array_equal(got[qsl[s], h], dv[s][0, h].astype(np.float64))
+
+
+def pin_prefill_chunking_invariance():
+    """Prefilling a sequence in two chunks gives the rows of one whole prefill,
+    and keys after a query's position never change its output."""
+    rng = np.random.default_rng(33)
+    n, a = 29, 12
+    q, kc, vc, bt, cl, qsl, dk, dv = _prefill_case(rng, 4, 2, 8, 4, [n], [n])
+    whole = O.ref_prefill(q, kc, vc, bt, cl, qsl, 0.35, "f32")
+    first = O.ref_prefill(q[:a], kc, vc, bt, np.array([a]), np.array([0, a]), 0.35, "f32")
+    second = O.ref_prefill(q[a:], kc, vc, bt, cl, np.array([0, n - a]), 0.35, "f32")
+    assert np.array_equal(np.concatenate([first, second]), whole)
+    # overwrite the rows after position 20 with other values
+    kc2, vc2 = kc.copy(), vc.copy()
+    for i in range(21, n):
+        kc2[bt[0, i // 4], :, i % 4] = 7.0
+        vc2[bt[0, i // 4], :, i % 4] = -3.0
+    moved = O.ref_prefill(q, kc2, vc2, bt, cl, qsl, 0.35, "f32")
+    assert np.array_equal(moved[:21], whole[:21])
+    assert not np.allclose(moved[21:], whole[21:])
+
+
+def pin_prefill_flop_count():
+    """Closed form: a whole-sequence causal prefill of n tokens sees
+    n(n+1)/2 (query, key) pairs; [OPS]'s [1, 32, 8192, 64] call does
+    4 * 64 * 32 * 8192 * 8193 / 2 flops."""
+    assert O.prefill_flops([8192], [0, 8192], 32, 64) == 4 * 64 * 32 * 8192 * 8193 // 2
+    # a chunk of 3 after 5 cached tokens: positions 5, 6, 7 see 6 + 7 + 8 keys
+    assert O.prefill_flops([8], [0, 3], 1, 1) == 4 * (6 + 7 + 8)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -381,7 +468,22 @@ def _right_aligned_gather(cache, table_row, context_len, kv_head, dtype):
     return O.to_f64(cache[blocks, kv_head, offs, :], dtype)
 
 
+def _chunk_at_start(context_len, chunk_len, t):
+    return t
+
+
+def _causal_off_by_one(position):
+    return position
+
+
+def _causal_one_too_many(position):
+    return position + 2
+
+
 MUTANTS = {
+    "prefill_chunk_at_start": ("query_position", _chunk_at_start),
+    "prefill_excludes_own_key": ("visible_keys", _causal_off_by_one),
+    "prefill_sees_next_key": ("visible_keys", _causal_one_too_many),
     "softmax_sign": ("softmax", _wrong_softmax_sign),
     "softmax_unnormalised": ("softmax", _unnormalised_softmax),
     "k_v_swapped": ("attend", _keys_and_values_swapped),
