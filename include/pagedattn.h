@@ -238,6 +238,42 @@ int32_t pa_swap_blocks(const void *src_k, const void *src_v, void *dst_k, void *
                        int32_t src_num_blocks, int32_t dst_num_blocks,
                        int32_t dtype, void *stream);
 
+/*
+ * pa_prefill - multi-token (chunked-prefill) paged attention: each query token
+ * of a chunk attends to its sequence's cached tokens up to and including its
+ * own position ([INFRA] §1.1, the per-step attention, for every token of the
+ * chunk; [OPS] calls the operator with a whole sequence of queries).
+ *
+ * Queries of all sequences are packed along one token axis:
+ *   q, out           [num_tokens, num_q_heads, head_dim], dtype
+ *   query_start_loc  int32 [num_seqs + 1]: sequence s owns tokens
+ *                    query_start_loc[s] .. query_start_loc[s+1]-1 (its chunk,
+ *                    L_s tokens; 0 <= L_s <= max_query_len)
+ *   context_lens     int32 [num_seqs]: cached tokens of sequence s INCLUDING
+ *                    the chunk, whose K/V must already be in the pools
+ *                    (pa_reshape_and_cache); L_s <= context_lens[s]
+ *   k_cache, v_cache, block_tables, num_blocks, max_blocks_per_seq as for
+ *   pa_decode.
+ * Token t of sequence s sits at position context_lens[s] - L_s + t and
+ * attends to positions 0 .. context_lens[s] - L_s + t; query head h reads KV
+ * head h / (num_q_heads / num_kv_heads). out = softmax(scale * q.K^T) V per
+ * (token, head), accumulated in fp32 and rounded once to dtype.
+ *
+ * Built: dtype PA_F16 or PA_BF16, head_dim 64 or 128, block_size 8-64,
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8}; otherwise PA_ERR_UNSUPPORTED.
+ * No workspace; nothing allocated. Device-resident preconditions (monotone
+ * query_start_loc ending at num_tokens, chunk and context lengths, table
+ * entries in range) are checked only under PA_DEBUG=1 (PA_ERR_BAD_INDEX).
+ * Tokens of sequences with L_s = 0 do not exist; nothing else is written.
+ */
+int32_t pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
+                   const int32_t *block_tables, const int32_t *context_lens,
+                   const int32_t *query_start_loc, float scale, int32_t num_seqs,
+                   int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                   int32_t max_blocks_per_seq, int32_t max_query_len, int32_t dtype,
+                   void *stream);
+
 /* A static, human-readable name of a status code. */
 const char *pa_status_str(int32_t status);
 

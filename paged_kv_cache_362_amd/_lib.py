@@ -29,6 +29,8 @@ SIGNATURES = {
     "pa_copy_blocks": (_i32, [_ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _i32, _i32, _ptr]),
     "pa_swap_blocks": (_i32, [_ptr, _ptr, _ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _i32,
                               _i32, _i32, _ptr]),
+    "pa_prefill": (_i32, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, ctypes.c_float, _i32, _i32,
+                          _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _ptr]),
     "pa_status_str": (ctypes.c_char_p, [_i32]),
     "pa_abi_version": (_i32, []),
 }

@@ -15,6 +15,7 @@
 
 #include "pa_blocks.h"
 #include "pa_internal.h"
+#include "pa_prefill.h"
 #include "pagedattn.h"
 
 namespace {
@@ -330,6 +331,71 @@ int32_t pa_swap_blocks(const void *src_k, const void *src_v, void *dst_k, void *
   p.dst_blocks = dst_num_blocks;
   p.block_bytes = int64_t(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
   return pa::launch_copy_blocks(p, s) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int32_t pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
+                   const int32_t *block_tables, const int32_t *context_lens,
+                   const int32_t *query_start_loc, float scale, int32_t num_seqs,
+                   int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                   int32_t max_blocks_per_seq, int32_t max_query_len, int32_t dtype,
+                   void *stream) {
+  if (num_seqs < 0 || num_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0 || max_query_len < 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return PA_ERR_BAD_SHAPE;
+  if (dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!block_size_ok(block_size) || !group_ok(num_q_heads / num_kv_heads))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (max_query_len > num_tokens) return PA_ERR_BAD_SHAPE;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
+    return PA_ERR_NULL_POINTER;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_UNSUPPORTED;
+  const int64_t group = num_q_heads / num_kv_heads;
+  const int64_t q_tiles = (int64_t(max_query_len) * group + pa::kPrefillRows - 1) / pa::kPrefillRows;
+  if (int64_t(num_seqs) * num_kv_heads * q_tiles > (int64_t(1) << 31) - 8) return PA_ERR_BAD_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    std::vector<int32_t> qsl(size_t(num_seqs) + 1), lens(num_seqs),
+        tab(size_t(num_seqs) * max_blocks_per_seq);
+    int32_t st = sync_copy_to_host(qsl.data(), query_start_loc, sizeof(int32_t) * qsl.size(), s);
+    if (st == PA_OK) st = sync_copy_to_host(lens.data(), context_lens, sizeof(int32_t) * lens.size(), s);
+    if (st == PA_OK) st = sync_copy_to_host(tab.data(), block_tables, sizeof(int32_t) * tab.size(), s);
+    if (st != PA_OK) return st;
+    if (qsl[0] != 0 || qsl[num_seqs] != num_tokens) return PA_ERR_BAD_INDEX;
+    for (int32_t i = 0; i < num_seqs; ++i) {
+      const int32_t chunk = qsl[i + 1] - qsl[i], n = lens[i];
+      if (chunk < 0 || chunk > max_query_len || n < chunk ||
+          int64_t(n) > int64_t(max_blocks_per_seq) * block_size)
+        return PA_ERR_BAD_INDEX;
+      if (chunk > 0 && n < 1) return PA_ERR_BAD_INDEX;
+      for (int32_t b = 0; b < (n + block_size - 1) / block_size; ++b) {
+        const int32_t id = tab[size_t(i) * max_blocks_per_seq + b];
+        if (id < 0 || id >= num_blocks) return PA_ERR_BAD_INDEX;
+      }
+    }
+  }
+  pa::PrefillParams p{};
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.query_start_loc = query_start_loc;
+  p.scale_log2 = float(double(scale) * 1.4426950408889634074);
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.block_size = block_size;
+  p.block_shift = __builtin_ctz(unsigned(block_size));
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.q_tiles = int(q_tiles);
+  return pa::launch_prefill(p, dtype, head_dim, max_query_len, s) == hipSuccess ? PA_OK
+                                                                               : PA_ERR_HIP;
 }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

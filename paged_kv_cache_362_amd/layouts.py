@@ -182,7 +182,7 @@ def make_paged_batch(*, num_q_heads: int, num_kv_heads: int, head_dim: int, dtyp
                      num_blocks: int | None = None, pool_slack: float = 0.25,
                      shared_prefix_seqs: int = 0, shared_prefix_tokens: int = 0,
                      fresh_block_write: bool = False, extra_table_cols: int = 0,
-                     shuffle_pool: bool = True,
+                     shuffle_pool: bool = True, poison_write_slots: bool = True,
                      rng: np.random.Generator | None = None, name: str = "") -> PagedBatch:
     """Build one decode step's inputs.
 
@@ -194,6 +194,8 @@ def make_paged_batch(*, num_q_heads: int, num_kv_heads: int, head_dim: int, dtyp
     per sequence at position n-1. ``shuffle_pool=False`` hands out blocks in
     ascending order, so each request's blocks are contiguous in the pool (the
     permutation is still drawn, so every value matches the shuffled layout).
+    With ``poison``, slots no sequence uses hold NaN, and so do the step's
+    write slots unless ``poison_write_slots`` is False.
     """
     if rng is None:
         rng = np.random.default_rng(seed)
@@ -256,8 +258,9 @@ def make_paged_batch(*, num_q_heads: int, num_kv_heads: int, head_dim: int, dtyp
             for pos in range(int(lens[s])):
                 blk = t.blocks[pos // block_size]
                 live[blk, pos % block_size] = True
-        for slot in slots:
-            live[slot // block_size, slot % block_size] = False
+        if poison_write_slots:
+            for slot in slots:
+                live[slot // block_size, slot % block_size] = False
         dead_blk, dead_off = np.nonzero(~live)
         nv = nan_value(dtype)
         k_cache[dead_blk, :, dead_off, :] = nv
@@ -271,6 +274,63 @@ def make_paged_batch(*, num_q_heads: int, num_kv_heads: int, head_dim: int, dtyp
         scale=float(np.float32(1.0 / math.sqrt(head_dim))), seed=seed,
         poisoned=poison, unique_blocks=len(used), name=name,
         meta={"pad_block": pad_block, "order": order})
+
+
+@dataclass
+class PrefillBatch:
+    """Host arrays of one multi-token (chunked-prefill) call: the paged pools
+    and tables of ``paged`` (their cache already holds every chunk's K/V) and
+    the packed queries of the chunks."""
+
+    paged: PagedBatch
+    q: np.ndarray                 # [T, Hq, D]
+    query_start_loc: np.ndarray   # [S + 1] int32
+    chunk_lens: np.ndarray        # [S] int32
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.chunk_lens.max()) if self.chunk_lens.size else 0
+
+    def __getattr__(self, name):  # pools, tables, lengths, dtype ... of the paged batch
+        if name == "paged":
+            raise AttributeError(name)
+        return getattr(self.paged, name)
+
+
+def make_prefill_batch(*, num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: str,
+                       block_size: int, context_lens, chunk_lens, seed: int,
+                       poison: bool = False, **kw) -> PrefillBatch:
+    """Pools and tables as ``make_paged_batch`` builds them for ``context_lens``,
+    then the packed queries of chunks of ``chunk_lens[s]`` tokens ending each
+    sequence's context (drawn after everything else)."""
+    rng = np.random.default_rng(seed)
+    paged = make_paged_batch(num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                             head_dim=head_dim, dtype=dtype, block_size=block_size,
+                             context_lens=context_lens, seed=seed, poison=poison, rng=rng,
+                             poison_write_slots=False, **kw)
+    chunks = np.asarray(chunk_lens(paged.context_lens, rng) if callable(chunk_lens)
+                        else chunk_lens, dtype=np.int32)
+    if chunks.shape != paged.context_lens.shape or (chunks > paged.context_lens).any() \
+            or (chunks < 0).any():
+        raise ValueError("one chunk length per sequence, 0 <= chunk <= context")
+    qsl = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    q = draw(rng, (int(qsl[-1]), num_q_heads, head_dim), dtype)
+    return PrefillBatch(paged=paged, q=q, query_start_loc=qsl, chunk_lens=chunks)
+
+
+# Multi-token workloads: [OPS]'s example call, [1, 32, 8192, 64] in fp16 with
+# 16-token blocks (512 blocks), as a whole-sequence prefill and as the last of
+# four 2048-token chunks.
+PREFILL_WORKLOADS = {
+    "ops_prefill_8192": dict(num_q_heads=32, num_kv_heads=32, head_dim=64, dtype="f16",
+                             block_size=16, context_lens=[8192], chunk_lens=[8192]),
+    "ops_chunk_2048_of_8192": dict(num_q_heads=32, num_kv_heads=32, head_dim=64, dtype="f16",
+                                   block_size=16, context_lens=[8192], chunk_lens=[2048]),
+}
+
+
+def make_prefill_workload(name: str, seed: int = 7) -> PrefillBatch:
+    return make_prefill_batch(seed=seed, name=name, **PREFILL_WORKLOADS[name])
 
 
 def make_config(config: int, seed: int | None = None, poison: bool = False) -> PagedBatch:
@@ -324,6 +384,15 @@ def to_torch(a: np.ndarray, dtype: str):
     if dtype == "bf16":
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
     return torch.from_numpy(a)
+
+
+def prefill_to_device(b: PrefillBatch, device="cuda"):
+    """torch tensors of a prefill batch on ``device``."""
+    t = to_device(b.paged, device)
+    t["q"] = to_torch(b.q, b.dtype).to(device)
+    import torch
+    t["query_start_loc"] = torch.from_numpy(b.query_start_loc).to(device)
+    return t
 
 
 def to_device(batch: PagedBatch, device="cuda"):

@@ -221,3 +221,36 @@ def swap_blocks(src_k: torch.Tensor, src_v: torch.Tensor, dst_k: torch.Tensor,
                                 block_mapping.shape[0], hkv, d, bs, src_k.shape[0],
                                 dst_k.shape[0], dtype_code(src_k.dtype), _stream(block_mapping))
     _check("pa_swap_blocks", code)
+
+
+def prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+            block_tables: torch.Tensor, context_lens: torch.Tensor,
+            query_start_loc: torch.Tensor, scale: float, max_query_len: int,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """Chunked-prefill paged attention (``pa_prefill``): q [T, Hq, D] packs the
+    chunks of all sequences (sequence s owns tokens query_start_loc[s] ..
+    query_start_loc[s+1]-1, the last tokens of its context_lens[s] cached
+    ones); each token attends causally to its sequence's cache."""
+    _on_gpu(q, k_cache, v_cache, block_tables, context_lens, query_start_loc)
+    _require(q.dim() == 3 and k_cache.dim() == 4 and k_cache.shape == v_cache.shape,
+             "q must be [T, Hq, D] and the pools [N, Hkv, B, D]")
+    for t in (q, k_cache, v_cache, block_tables, context_lens, query_start_loc):
+        _require(t.is_contiguous(), "all tensors must be contiguous")
+    _require(q.dtype == k_cache.dtype == v_cache.dtype, "q and the pools share one dtype")
+    for t in (block_tables, context_lens, query_start_loc):
+        _require(t.dtype == torch.int32, "tables, lengths and query_start_loc are int32")
+    s = context_lens.shape[0]
+    _require(query_start_loc.shape == (s + 1,) and block_tables.dim() == 2 and
+             block_tables.shape[0] == s, "query_start_loc [S+1], block_tables [S, M]")
+    n, hkv, bs, d = k_cache.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous(),
+             "out must match q")
+    code = lib().pa_prefill(
+        _dev_ptr(out), _dev_ptr(q), _dev_ptr(k_cache), _dev_ptr(v_cache),
+        _dev_ptr(block_tables), _dev_ptr(context_lens), _dev_ptr(query_start_loc), float(scale),
+        s, q.shape[0], q.shape[1], hkv, d, bs, n, block_tables.shape[1], int(max_query_len),
+        dtype_code(q.dtype), _stream(q))
+    _check("pa_prefill", code)
+    return out

@@ -165,3 +165,30 @@ def test_swap_blocks_rejects_bad_arguments_before_launch(lib):
     assert f(16, 16, 16, 16, 16, 1, 4, 64, 16, 8, 8, 7, None) == UNSUP
     assert f(16, 16, 24, 16, 16, 1, 4, 64, 16, 8, 8, F16, None) == UNSUP  # misaligned
     assert f(None, None, None, None, None, 0, 4, 64, 16, 8, 8, F16, None) == OK
+
+
+def test_prefill_rejects_bad_arguments_before_launch(lib):
+    f = lib.pa_prefill
+    #        out q   k   v   tab len qsl  scale S  T  Hq Hkv D   B   N   M  Lmax dtype
+    ok = [16, 16, 16, 16, 16, 16, 16, 0.125, 2, 10, 8, 2, 64, 16, 8, 4, 8, F16, None]
+
+    def call(**kw):
+        a = list(ok)
+        names = ["out", "q", "k", "v", "tab", "len", "qsl", "scale", "S", "T", "Hq", "Hkv", "D",
+                 "B", "N", "M", "Lmax", "dtype", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(out=None) == NULLP
+    assert call(qsl=None) == NULLP
+    assert call(Hq=6, Hkv=4) == SHAPE
+    assert call(S=-1) == SHAPE
+    assert call(Lmax=11) == SHAPE            # longer than the tokens given
+    assert call(dtype=0) == UNSUP            # f32 is not built
+    assert call(D=256) == UNSUP
+    assert call(B=12) == UNSUP
+    assert call(Hq=6, Hkv=2) == UNSUP        # group 3
+    assert call(q=24) == UNSUP               # misaligned
+    assert call(T=0, out=None, q=None) == OK  # nothing to do
+    assert call(Lmax=0, out=None) == OK

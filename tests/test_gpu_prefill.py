@@ -1,0 +1,124 @@
+"""GPU parity of multi-token (chunked-prefill) paged attention, pa_prefill,
+against the float64 oracle ([INFRA] "【infra之路】10-PagedAttention 与 KV Cache
+管理" §1.1 for every token of a chunk; [OPS]'s [1, 32, 8192, 64] call).
+
+Small cases are compared element by element with ``ref_prefill``. The full
+[OPS] shape is compared on sampled (token, head) rows: a token at position p
+sees exactly what a decode step with context p + 1 sees, so each sampled row
+is checked with the decode oracle over a context of p + 1 tokens.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.paged_attention as O
+from paged_kv_cache_362_amd import layouts, ops
+from parity import assert_decode_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(b: layouts.PrefillBatch, t=None):
+    t = t or layouts.prefill_to_device(b)
+    out = ops.prefill(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                      t["query_start_loc"], b.scale, b.max_query_len)
+    torch.cuda.synchronize()
+    return layouts.from_device(out, b.dtype)
+
+
+def _oracle(b: layouts.PrefillBatch):
+    return O.ref_prefill(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens,
+                         b.query_start_loc, b.scale, b.dtype)
+
+
+CASES = [
+    # dtype, Hq, Hkv, D, B, context_lens, chunk_lens
+    ("f16", 4, 4, 64, 16, [300], [300]),                 # whole prefill, ragged tiles
+    ("f16", 8, 8, 128, 16, [333, 70], [45, 70]),          # chunk after a prefix + whole
+    ("bf16", 8, 2, 128, 32, [257, 129, 40], [257, 1, 40]),  # GQA 4, a single-token chunk
+    ("bf16", 16, 2, 64, 8, [190, 64], [150, 64]),         # GQA 8, 8-token blocks
+    ("f16", 4, 2, 64, 64, [500, 3], [200, 3]),            # 64-token blocks
+    ("bf16", 2, 2, 128, 16, [161, 90, 33], [0, 90, 33]),  # an empty chunk
+    ("f16", 8, 4, 128, 16, [1, 2, 31, 32, 33], [1, 2, 31, 32, 33]),  # tile edges
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-h{c[1]}/{c[2]}-d{c[3]}-b{c[4]}-{c[6]}"
+                                             for c in CASES])
+def test_prefill_matches_oracle(case):
+    dtype, hq, hkv, d, bs, lens, chunks = case
+    b = layouts.make_prefill_batch(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, dtype=dtype,
+                                   block_size=bs, context_lens=lens, chunk_lens=chunks,
+                                   seed=sum(lens) + hq, poison=True)
+    got = _run(b)
+    assert_decode_close(got, _oracle(b), dtype, f"prefill {case}")
+
+
+def test_prefill_single_token_chunks_equal_decode():
+    """Chunks of one token are decode steps: pa_prefill and pa_decode agree
+    with the oracle (and each other) on the scaled GQA workload."""
+    pb = layouts.scaled_config(3, max_seqs=4, max_len=700)
+    b = layouts.PrefillBatch(paged=pb, q=pb.q, query_start_loc=np.arange(5, dtype=np.int32),
+                             chunk_lens=np.ones(4, np.int32))
+    got = _run(b)
+    want = O.ref_decode(pb.q, pb.k_cache, pb.v_cache, pb.block_tables, pb.context_lens,
+                        pb.scale, pb.dtype)
+    assert_decode_close(got, want, pb.dtype, "single-token chunks")
+
+
+def test_prefill_block_permutation_is_bit_identical():
+    b = layouts.make_prefill_batch(num_q_heads=8, num_kv_heads=2, head_dim=128, dtype="f16",
+                                   block_size=16, context_lens=[400, 220], chunk_lens=[130, 220],
+                                   seed=5)
+    base = _run(b)
+    perm = np.random.default_rng(6).permutation(b.num_blocks)
+    kc = np.empty_like(b.k_cache)
+    vc = np.empty_like(b.v_cache)
+    kc[perm] = b.k_cache
+    vc[perm] = b.v_cache
+    paged = layouts.PagedBatch(**{**b.paged.__dict__, "k_cache": kc, "v_cache": vc,
+                                  "block_tables": perm[b.block_tables].astype(np.int32)})
+    moved = _run(layouts.PrefillBatch(paged=paged, q=b.q, query_start_loc=b.query_start_loc,
+                                      chunk_lens=b.chunk_lens))
+    assert np.array_equal(moved.view(np.uint8), base.view(np.uint8))
+
+
+@pytest.mark.parametrize("name", sorted(layouts.PREFILL_WORKLOADS))
+def test_prefill_full_size_sampled_rows(name):
+    """[OPS]'s shape at full size, in the launch bench.py times; sampled rows
+    checked with the decode oracle at context p + 1."""
+    b = layouts.make_prefill_workload(name)
+    got = _run(b)
+    assert not np.isnan(O.to_f64(got, b.dtype)).any()
+    rng = np.random.default_rng(8)
+    n, chunk = int(b.context_lens[0]), int(b.chunk_lens[0])
+    toks = np.unique(np.concatenate([[0, 1, chunk - 1], rng.integers(0, chunk, 13)]))
+    for t in toks:
+        pos = n - chunk + int(t)
+        want = O.ref_decode(b.q[t:t + 1], b.k_cache, b.v_cache, b.block_tables[:1],
+                            np.array([pos + 1], np.int32), b.scale, b.dtype)
+        assert_decode_close(got[t:t + 1], want, b.dtype, f"{name} token {t} (position {pos})")
+
+
+def test_prefill_checks_in_debug_mode(monkeypatch):
+    b = layouts.make_prefill_batch(num_q_heads=4, num_kv_heads=4, head_dim=64, dtype="f16",
+                                   block_size=16, context_lens=[40, 20], chunk_lens=[10, 20],
+                                   seed=2)
+    t = layouts.prefill_to_device(b)
+    monkeypatch.setenv("PA_DEBUG", "1")
+    bad = {
+        "chunk longer than context": dict(context_lens=torch.tensor([40, 19], dtype=torch.int32)),
+        "start not 0": dict(query_start_loc=torch.tensor([1, 10, 30], dtype=torch.int32)),
+        "table entry out of range": dict(block_tables=torch.full_like(t["block_tables"], 10**6)),
+    }
+    for what, repl in bad.items():
+        args = {**t, **{k: v.cuda() for k, v in repl.items()}}
+        with pytest.raises(ops.PagedAttentionError) as e:
+            ops.prefill(args["q"], args["k_cache"], args["v_cache"], args["block_tables"],
+                        args["context_lens"], args["query_start_loc"], b.scale, b.max_query_len)
+        assert e.value.code == 6, what
+    # and a good call still passes under the checks
+    ops.prefill(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                t["query_start_loc"], b.scale, b.max_query_len)
+    torch.cuda.synchronize()
