@@ -60,6 +60,9 @@ def parse_args(argv=None):
     ap.add_argument("--paging-sweep", action="store_true",
                     help="decode on contiguous vs shuffled block tables at block sizes "
                          "8/16/32/64 (LLaMA-7B-layer shapes); prints one JSON line")
+    ap.add_argument("--prefill", action="store_true",
+                    help="chunked-prefill attention on the [1, 32, 8192, 64] fp16 call "
+                         "(whole sequence, and the last 2048-token chunk); one JSON line")
     ap.add_argument("--block-ops", action="store_true",
                     help="copy-on-write and swap block copies at LLaMA-7B-layer block shapes "
                          "beside plain contiguous copies of the same bytes; one JSON line")
@@ -163,6 +166,57 @@ def paging_sweep(args) -> dict:
     return {"paging_sweep": rows,
             "workload": "LLaMA-7B-layer MHA decode shapes (32 seqs, 32/32 heads, D 128, "
                         "fp16, lengths U[128, 2048]), balanced pa_decode",
+            "steps": args.steps, "warmup": args.warmup, "statistic": "median"}
+
+
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak
+
+
+def prefill_bench(args) -> dict:
+    """pa_prefill on the multi-token workloads; TFLOP/s of the causal
+    products against the dense fp16 MFMA peak (the bound once chunks are
+    long: 4 * L flop per K/V byte at fp16)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_362_amd import layouts, ops, sizing
+
+    dev = torch.device("cuda:0")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    rows = []
+    for name in sorted(layouts.PREFILL_WORKLOADS):
+        b = layouts.make_prefill_workload(name)
+        t = layouts.prefill_to_device(b, dev)
+        out = torch.empty_like(t["q"])
+
+        def call():
+            ops.prefill(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                        t["context_lens"], t["query_start_loc"], b.scale, b.max_query_len, out)
+        for _ in range(args.warmup):
+            flush.amax()
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for e0, e1 in ev:
+            flush.amax()
+            e0.record()
+            call()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+        flops = sizing.prefill_flops(b.context_lens, b.chunk_lens, b.num_q_heads, b.head_dim)
+        nbytes = sizing.prefill_algorithmic_bytes(b.context_lens, b.chunk_lens, b.num_q_heads,
+                                                  b.num_kv_heads, b.head_dim, b.elem_bytes,
+                                                  b.block_size)
+        tflops = flops / ms / 1e9
+        rows.append({"workload": name, "us": round(ms * 1e3, 1), "flops": flops,
+                     "TFLOPs": round(tflops, 1),
+                     "frac_of_mfma_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                     "algorithmic_bytes": nbytes, "GBps": round(nbytes / ms / 1e6, 1),
+                     "tokens_per_s": round(int(b.chunk_lens.sum()) / ms * 1e3, 1)})
+        del t, out
+        torch.cuda.empty_cache()
+    return {"prefill": rows, "peak_tflops": MFMA_F16_PEAK_TFLOPS, "bound": "mfma",
+            "shape": "[OPS] call [1, 32, 8192, 64] fp16, 16-token blocks, shuffled pool",
             "steps": args.steps, "warmup": args.warmup, "statistic": "median"}
 
 
@@ -274,6 +328,9 @@ def main(argv=None) -> int:
         return 0
     if args.block_ops:
         print(json.dumps(block_ops(args)), flush=True)
+        return 0
+    if args.prefill:
+        print(json.dumps(prefill_bench(args)), flush=True)
         return 0
 
     from paged_kv_cache_362_amd import layouts, ops, sizing

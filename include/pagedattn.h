@@ -260,7 +260,8 @@ int32_t pa_swap_blocks(const void *src_k, const void *src_v, void *dst_k, void *
  * (token, head), accumulated in fp32 and rounded once to dtype.
  *
  * Built: dtype PA_F16 or PA_BF16, head_dim 64 or 128, block_size 8-64,
- * num_q_heads / num_kv_heads in {1, 2, 4, 8}; otherwise PA_ERR_UNSUPPORTED.
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8}, a finite scale > 0; otherwise
+ * PA_ERR_UNSUPPORTED.
  * No workspace; nothing allocated. Device-resident preconditions (monotone
  * query_start_loc ending at num_tokens, chunk and context lengths, table
  * entries in range) are checked only under PA_DEBUG=1 (PA_ERR_BAD_INDEX).

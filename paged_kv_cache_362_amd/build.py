@@ -32,6 +32,14 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-source flags. The prefill kernel rescales its MFMA accumulators with
+# VALU code; with the accumulators in AGPRs the compiler copies all of them
+# to VGPRs and back on every key tile, so its MFMAs write VGPRs instead.
+SOURCE_FLAGS = {
+    "pa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -46,7 +54,8 @@ def sources() -> list[str]:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), []), "-c", src,
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

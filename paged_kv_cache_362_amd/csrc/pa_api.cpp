@@ -4,6 +4,7 @@
 // contract of every entry point are in include/pagedattn.h.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -346,6 +347,7 @@ int32_t pa_prefill(void *out, const void *q, const void *k_cache, const void *v_
     return PA_ERR_BAD_SHAPE;
   if (dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || scale == INFINITY) return PA_ERR_UNSUPPORTED;
   if (!block_size_ok(block_size) || !group_ok(num_q_heads / num_kv_heads))
     return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;

@@ -27,7 +27,10 @@
 // Computing the transposed scores puts each query row in one lane column, so
 // the softmax weights P^T feed the second product from the registers they are
 // in. The online softmax runs in the log2 domain with a running maximum per
-// row; the row sum is kept per lane and reduced once at the end.
+// row that is raised lazily (see kRescaleSlack); the row sum is kept per lane
+// and reduced once at the end. Scores are masked only in the tiles that cross
+// a row's position. The scale must be positive (the tile maximum is taken on
+// unscaled scores).
 //
 // Precision of P: fp16 weights carry 2^-11 relative error (the largest weight
 // is exactly 1), bf16 weights 2^-8, too much for a 2e-3 output bound, so the
@@ -42,6 +45,7 @@ namespace {
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kTileKeys = 32;
+constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay below 256
 
 template <int D, int QB> struct PfShape {
   static constexpr int KS = D / 32;                      // k-steps of the score product
@@ -77,11 +81,17 @@ template <> __device__ __forceinline__ f32x4 mfma16<PA_BF16>(const u32x4 &a, con
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Two floats -> one dword of two storage elements (round to nearest even).
-template <int DT> __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  using T = typename Store<DT>::T;
-  const T a = Store<DT>::cvt(lo), b = Store<DT>::cvt(hi);
-  return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+// Two floats -> two storage elements in one dword, round to nearest even, by
+// gfx950's packed conversions (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <int DT> __device__ __forceinline__ uint32_t cvt2(float lo, float hi);
+template <> __device__ __forceinline__ uint32_t cvt2<PA_F16>(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+}
+template <> __device__ __forceinline__ uint32_t cvt2<PA_BF16>(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // Storage element -> float (exact).
@@ -100,29 +110,58 @@ template <> __device__ __forceinline__ float unpack_hi<PA_BF16>(uint32_t w) {
   return __builtin_bit_cast(float, w & 0xffff0000u);
 }
 
-__device__ __forceinline__ float xor_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+// Maximum / sum over the 4 lanes l, l^16, l^32, l^48 (the lane groups that
+// hold one query row's keys). permlane16_swap hands each lane the values of
+// its row pair (rows 2r, 2r+1), permlane32_swap those of lanes l%32 and
+// 32 + l%32: two VALU exchanges, no LDS traffic. The pair's elements are
+// copied to scalars before any bit cast (a bit cast of a vector element
+// lvalue reads element 0 with this compiler).
+__device__ __forceinline__ void swap16(float v, float &a, float &b) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
 }
-__device__ __forceinline__ float xor_sum(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+__device__ __forceinline__ void swap32(float v, float &a, float &b) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float group_max(float v) {
+  float a, b;
+  swap16(v, a, b);
+  swap32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float group_sum(float v) {
+  float a, b;
+  swap16(v, a, b);
+  swap32(a + b, a, b);
+  return a + b;
 }
 
-// Global -> register staging of one key tile, and the table entries it needs.
-template <int D, int QB> struct Stager {
-  using S = PfShape<D, QB>;
+// One stage of the global -> LDS pipeline: the table entries and the K/V
+// chunks of one key tile, held in registers by every thread.
+template <int D> struct KVStage {
+  using S = PfShape<D, 2>;
+  int kphys[S::KCH_T], vphys[S::VIT_T];
+  u32x4 k[S::KCH_T], v0[S::VIT_T], v1[S::VIT_T];
+};
+
+// What each thread stages of a key tile, and how.
+template <int D> struct Stager {
+  using S = PfShape<D, 2>;
   const char *kbase;     // k_cache + kh * B * D elements, in bytes
   const char *vbase;
   const int32_t *table;  // this sequence's table row
   int64_t blk_bytes;     // Hkv * B * D * 2: one physical block of all KV heads
-  int row_bytes;         // D * 2
   int bshift, bmask;
   int n;                 // context length
   int kkey[S::KCH_T], kdc[S::KCH_T];   // K chunks of this thread
   int vkey[S::VIT_T], vdc[S::VIT_T];   // V (even key, chunk) items of this thread
-  int kphys[S::KCH_T], vphys[S::VIT_T];
-  u32x4 k[S::KCH_T], v0[S::VIT_T], v1[S::VIT_T];
 
   __device__ void init(int tid) {
 #pragma unroll
@@ -144,38 +183,38 @@ template <int D, int QB> struct Stager {
   // past the context read real data that the softmax then gives weight 0.
   __device__ __forceinline__ int pos_of(int j, int key) const { return min(j * kTileKeys + key, n - 1); }
 
-  __device__ void load_table(int j) {
+  __device__ void load_table(KVStage<D> &r, int j) const {
 #pragma unroll
-    for (int u = 0; u < S::KCH_T; ++u) kphys[u] = table[pos_of(j, kkey[u]) >> bshift];
+    for (int u = 0; u < S::KCH_T; ++u) r.kphys[u] = table[pos_of(j, kkey[u]) >> bshift];
 #pragma unroll
-    for (int u = 0; u < S::VIT_T; ++u) vphys[u] = table[pos_of(j, vkey[u]) >> bshift];
+    for (int u = 0; u < S::VIT_T; ++u) r.vphys[u] = table[pos_of(j, vkey[u]) >> bshift];
   }
-  __device__ void load_kv(int j) {
+  __device__ void load_kv(KVStage<D> &r, int j) const {
 #pragma unroll
     for (int u = 0; u < S::KCH_T; ++u) {
       const int pos = pos_of(j, kkey[u]);
-      const int64_t off = int64_t(kphys[u]) * blk_bytes + (pos & bmask) * row_bytes + kdc[u] * 16;
-      k[u] = *reinterpret_cast<const u32x4 *>(kbase + off);
+      const int64_t off = int64_t(r.kphys[u]) * blk_bytes + (pos & bmask) * (D * 2) + kdc[u] * 16;
+      r.k[u] = *reinterpret_cast<const u32x4 *>(kbase + off);
     }
 #pragma unroll
     for (int u = 0; u < S::VIT_T; ++u) {
       // The two keys of a pair are in one block (even key, block size >= 8).
       const int p0 = pos_of(j, vkey[u]), p1 = pos_of(j, vkey[u] + 1);
-      const int64_t b = int64_t(vphys[u]) * blk_bytes + vdc[u] * 16;
-      v0[u] = *reinterpret_cast<const u32x4 *>(vbase + b + (p0 & bmask) * row_bytes);
-      v1[u] = *reinterpret_cast<const u32x4 *>(vbase + b + (p1 & bmask) * row_bytes);
+      const int64_t b = int64_t(r.vphys[u]) * blk_bytes + vdc[u] * 16;
+      r.v0[u] = *reinterpret_cast<const u32x4 *>(vbase + b + (p0 & bmask) * (D * 2));
+      r.v1[u] = *reinterpret_cast<const u32x4 *>(vbase + b + (p1 & bmask) * (D * 2));
     }
   }
-  __device__ void store_lds(char *buf) const {
+  __device__ void store_lds(const KVStage<D> &r, char *buf) const {
 #pragma unroll
     for (int u = 0; u < S::KCH_T; ++u)
-      *reinterpret_cast<u32x4 *>(buf + kkey[u] * S::KPITCH + kdc[u] * 16) = k[u];
+      *reinterpret_cast<u32x4 *>(buf + kkey[u] * S::KPITCH + kdc[u] * 16) = r.k[u];
 #pragma unroll
     for (int u = 0; u < S::VIT_T; ++u) {
       char *col = buf + S::KBYTES + v_slot(vkey[u]) * 2;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t a = v0[u][w], b = v1[u][w];
+        const uint32_t a = r.v0[u][w], b = r.v1[u][w];
         // dims 8*dc + 2w and 8*dc + 2w + 1: (key, key + 1) pairs of each
         const uint32_t even = __builtin_amdgcn_perm(b, a, 0x05040100u);
         const uint32_t odd = __builtin_amdgcn_perm(b, a, 0x07060302u);
@@ -186,7 +225,7 @@ template <int D, int QB> struct Stager {
   }
 };
 
-template <int DT, int D, int G, int QB>
+template <int DT, int D, int G, int QB, int NSET>
 __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams p) {
   using S = PfShape<D, QB>;
   extern __shared__ __align__(16) char lds[];
@@ -229,16 +268,16 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams p) {
       qreg[qb][ks] = valid ? v : u32x4{0, 0, 0, 0};
     }
   }
+  const int wave_min_qpos = n - L + (qt * S::ROWS + wave * QB * 16) / G;
   const int r_last = min(rows, (qt + 1) * S::ROWS) - 1;
   const int last_pos = n - L + r_last / G;
   const int ntiles = last_pos / kTileKeys + 1;
 
-  Stager<D, QB> st;
+  Stager<D> st;
   st.kbase = reinterpret_cast<const char *>(p.k_cache) + int64_t(kh) * p.block_size * D * 2;
   st.vbase = reinterpret_cast<const char *>(p.v_cache) + int64_t(kh) * p.block_size * D * 2;
   st.table = p.block_tables + int64_t(seq) * p.max_blocks_per_seq;
   st.blk_bytes = int64_t(p.num_kv_heads) * p.block_size * D * 2;
-  st.row_bytes = D * 2;
   st.bshift = p.block_shift;
   st.bmask = p.block_size - 1;
   st.n = n;
@@ -254,93 +293,128 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams p) {
     for (int db = 0; db < S::DB; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // Pipeline of NSET register stages: at the top of iteration j, stage
+  // (j + i) % NSET holds the loads in flight for tile j + i (0 < i < NSET),
+  // stage j % NSET is free and holds the table entries of tile j + NSET, and
+  // LDS buffer j & 1 holds tile j. Tiles past the last are clamped to it, and
+  // iterations past it compute with every key masked (no effect), so the loop
+  // runs a multiple of NSET iterations with compile-time stage indices.
   const int last = ntiles - 1;
-  st.load_table(0);
-  st.load_kv(0);
-  st.load_table(min(1, last));
-  st.store_lds(lds);
+  KVStage<D> R[NSET];
+#pragma unroll
+  for (int i = 0; i < NSET; ++i) st.load_table(R[i], min(i, last));
+#pragma unroll
+  for (int i = 0; i < NSET; ++i) st.load_kv(R[i], min(i, last));
+  st.store_lds(R[0], lds);
+  st.load_table(R[0], min(NSET, last));
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    // Next tile's loads are in flight while this one is computed. The last
-    // iteration reloads tile `last` into the idle buffer (never read).
-    st.load_kv(min(j + 1, last));
-    st.load_table(min(j + 2, last));
-    const char *kb_lds = lds + (j & 1) * S::BUF;
-    const char *vt_lds = kb_lds + S::KBYTES;
+  for (int j0 = 0; j0 < ntiles; j0 += NSET) {
+#pragma unroll
+    for (int u = 0; u < NSET; ++u) {
+      const int j = j0 + u;
+      KVStage<D> &mine = R[u];                  // free: gets tile j + NSET
+      KVStage<D> &next = R[(u + 1) % NSET];     // tile j + 1, in flight
+      st.load_kv(mine, min(j + NSET, last));
+      st.load_table(next, min(j + NSET + 1, last));
+      const bool live = j < ntiles;
+      const char *kb_lds = lds + (j & 1) * S::BUF;
+      const char *vt_lds = kb_lds + S::KBYTES;
 
-    // S^T = K . Q^T for 2 blocks of 16 keys.
-    f32x4 s[QB][2];
+      // S^T = K . Q^T for 2 blocks of 16 keys.
+      f32x4 s[QB][2];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) s[qb][0] = s[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int qb = 0; qb < QB; ++qb) s[qb][0] = s[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks) {
+      for (int ks = 0; ks < S::KS; ++ks) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(kb_lds + (16 * kb + lr) * S::KPITCH +
-                                                           (32 * ks + 8 * lg) * 2);
+        for (int kb = 0; kb < 2; ++kb) {
+          const u32x4 a = *reinterpret_cast<const u32x4 *>(kb_lds + (16 * kb + lr) * S::KPITCH +
+                                                             (32 * ks + 8 * lg) * 2);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma16<DT>(a, qreg[qb][ks], s[qb][kb]);
-      }
-    }
-
-    // Online softmax per query row (lane column), and P^T in storage form.
-    u32x4 ph[QB], pl[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float x[8];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int key = j * kTileKeys + 16 * kb + 4 * lg + jj;
-          const float v = s[qb][kb][jj] * p.scale_log2;
-          x[4 * kb + jj] = key <= qpos[qb] ? v : -INFINITY;
+          for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma16<DT>(a, qreg[qb][ks], s[qb][kb]);
         }
-      float mx = x[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-      mx = xor_max(mx);
-      const float m_new = fmaxf(m[qb], mx);
-      const float alpha = fast_exp2(m[qb] - m_new);
-      m[qb] = m_new;
-      float e[8], sum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        e[i] = fast_exp2(x[i] - m_new);
-        sum += e[i];
       }
-      l[qb] = l[qb] * alpha + sum;
-#pragma unroll
-      for (int db = 0; db < S::DB; ++db) acc[qb][db] *= alpha;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t hw = pack2<DT>(e[2 * w], e[2 * w + 1]);
-        ph[qb][w] = hw;
-        if (DT == PA_BF16)
-          pl[qb][w] = pack2<DT>(e[2 * w] - unpack_lo<DT>(hw), e[2 * w + 1] - unpack_hi<DT>(hw));
-      }
-    }
 
-    // O^T += V^T . P^T
+      // Mask keys past each row's position (and every key of the iterations
+      // past the last tile). Only tiles that reach past the wave's first row
+      // need it; the branch is uniform across the wave.
+      if (!live || j * kTileKeys + kTileKeys - 1 > wave_min_qpos) {
 #pragma unroll
-    for (int db = 0; db < S::DB; ++db) {
-      const u32x4 a = *reinterpret_cast<const u32x4 *>(vt_lds + (16 * db + lr) * S::VPITCH + 16 * lg);
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int key = j * kTileKeys + 16 * kb + 4 * lg + jj;
+              if (!(live && key <= qpos[qb])) s[qb][kb][jj] = -INFINITY;
+            }
+      }
+
+      // Online softmax per query row (lane column). The running maximum m is
+      // only raised when a row's tile maximum exceeds it by more than
+      // kRescaleSlack (log2 units): weights then stay below 2^kRescaleSlack,
+      // well inside fp16/bf16 range, and the rescale of the accumulators (a
+      // branch uniform across the wave) is rare after the first tile.
+      float tmax[QB];
+      bool raise = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        acc[qb][db] = mfma16<DT>(a, ph[qb], acc[qb][db]);
-        if (DT == PA_BF16) acc[qb][db] = mfma16<DT>(a, pl[qb], acc[qb][db]);
+        float mx = fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), fmaxf(s[qb][0][2], s[qb][0][3]));
+        mx = fmaxf(mx, fmaxf(fmaxf(s[qb][1][0], s[qb][1][1]), fmaxf(s[qb][1][2], s[qb][1][3])));
+        tmax[qb] = group_max(mx) * p.scale_log2;
+        raise |= tmax[qb] > m[qb] + kRescaleSlack;
       }
-    }
+      if (__any(raise)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float m_new = fmaxf(m[qb], tmax[qb]);
+          const float alpha = fast_exp2(m[qb] - m_new);
+          m[qb] = m_new;
+          l[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < S::DB; ++db) acc[qb][db] *= alpha;
+        }
+      }
+      u32x4 ph[QB], pl[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float e[8];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            e[4 * kb + jj] = fast_exp2(fmaf(s[qb][kb][jj], p.scale_log2, -m[qb]));
+        l[qb] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t hw = cvt2<DT>(e[2 * w], e[2 * w + 1]);
+          ph[qb][w] = hw;
+          if (DT == PA_BF16)
+            pl[qb][w] = cvt2<DT>(e[2 * w] - unpack_lo<DT>(hw), e[2 * w + 1] - unpack_hi<DT>(hw));
+        }
+      }
 
-    st.store_lds(lds + ((j + 1) & 1) * S::BUF);
-    __syncthreads();
+      // O^T += V^T . P^T
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db) {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(vt_lds + (16 * db + lr) * S::VPITCH + 16 * lg);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          acc[qb][db] = mfma16<DT>(a, ph[qb], acc[qb][db]);
+          if (DT == PA_BF16) acc[qb][db] = mfma16<DT>(a, pl[qb], acc[qb][db]);
+        }
+      }
+
+      st.store_lds(next, lds + ((j + 1) & 1) * S::BUF);
+      __syncthreads();
+    }
   }
 
   // out = acc / l for the valid rows.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float inv = 1.f / xor_sum(l[qb]);
+    const float inv = 1.f / group_sum(l[qb]);
     const int r = qt * S::ROWS + (wave * QB + qb) * 16 + lr;
     const int t = r / G;
     if (t >= L) continue;
@@ -350,8 +424,8 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams p) {
     for (int db = 0; db < S::DB; ++db) {
       const f32x4 o = acc[qb][db] * inv;
       uint2 w;
-      w.x = pack2<DT>(o[0], o[1]);
-      w.y = pack2<DT>(o[2], o[3]);
+      w.x = cvt2<DT>(o[0], o[1]);
+      w.y = cvt2<DT>(o[2], o[3]);
       *reinterpret_cast<uint2 *>(orow + (16 * db + 4 * lg) * 2) = w;
     }
   }
@@ -360,11 +434,12 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams p) {
 template <int DT, int D, int G>
 hipError_t launch_g(const PrefillParams &p, hipStream_t stream) {
   constexpr int QB = 2;
+  constexpr int NSET = D == 64 ? 3 : 2;
   using S = PfShape<D, QB>;
   const int64_t items = int64_t(p.num_seqs) * p.num_kv_heads * p.q_tiles;
   if (items == 0) return hipSuccess;
   const int64_t grid = (items + 7) / 8 * 8;
-  hipLaunchKernelGGL((prefill_kernel<DT, D, G, QB>), dim3(unsigned(grid)), dim3(kPfThreads),
+  hipLaunchKernelGGL((prefill_kernel<DT, D, G, QB, NSET>), dim3(unsigned(grid)), dim3(kPfThreads),
                      2 * S::BUF, stream, p);
   return hipGetLastError();
 }

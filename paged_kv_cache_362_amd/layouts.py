@@ -320,8 +320,11 @@ def make_prefill_batch(*, num_q_heads: int, num_kv_heads: int, head_dim: int, dt
 
 # Multi-token workloads: [OPS]'s example call, [1, 32, 8192, 64] in fp16 with
 # 16-token blocks (512 blocks), as a whole-sequence prefill and as the last of
-# four 2048-token chunks.
+# four 2048-token chunks; and a LLaMA-7B layer's heads (32 x 128, fp16) over a
+# 4096-token prompt.
 PREFILL_WORKLOADS = {
+    "llama7b_prefill_4096": dict(num_q_heads=32, num_kv_heads=32, head_dim=128, dtype="f16",
+                                 block_size=16, context_lens=[4096], chunk_lens=[4096]),
     "ops_prefill_8192": dict(num_q_heads=32, num_kv_heads=32, head_dim=64, dtype="f16",
                              block_size=16, context_lens=[8192], chunk_lens=[8192]),
     "ops_chunk_2048_of_8192": dict(num_q_heads=32, num_kv_heads=32, head_dim=64, dtype="f16",

@@ -95,3 +95,27 @@ def internal_fragmentation(context_lens: Sequence[int], block_size: int) -> floa
     used = sum(int(n) for n in context_lens)
     allocated = sum(blocks_needed(int(n), block_size) * block_size for n in context_lens)
     return 0.0 if allocated == 0 else (allocated - used) / allocated
+
+
+def prefill_flops(context_lens: Sequence[int], chunk_lens: Sequence[int], num_q_heads: int,
+                  head_dim: int) -> int:
+    """Flops of a causal chunked prefill: a chunk of L tokens ending a context
+    of n sees n - L + 1, ..., n keys per token and head; each (token, head,
+    key) costs 2 * D for the score and 2 * D for the weighted value."""
+    pairs = 0
+    for n, chunk in zip(context_lens, chunk_lens):
+        n, chunk = int(n), int(chunk)
+        pairs += chunk * (n - chunk) + chunk * (chunk + 1) // 2
+    return 4 * head_dim * num_q_heads * pairs
+
+
+def prefill_algorithmic_bytes(context_lens: Sequence[int], chunk_lens: Sequence[int],
+                              num_q_heads: int, num_kv_heads: int, head_dim: int,
+                              elem_bytes: int, block_size: int) -> int:
+    """Bytes a chunked prefill must move at least once: the K and V rows of
+    every cached token, the queries and outputs of every chunk token, the
+    table entries and the lengths and chunk starts."""
+    kv = sum(int(n) for n in context_lens) * num_kv_heads * head_dim * 2 * elem_bytes
+    q_and_out = 2 * sum(int(c) for c in chunk_lens) * num_q_heads * head_dim * elem_bytes
+    tables = 4 * sum(blocks_needed(int(n), block_size) for n in context_lens)
+    return kv + q_and_out + tables + 8 * len(context_lens) + 4

@@ -190,5 +190,8 @@ def test_prefill_rejects_bad_arguments_before_launch(lib):
     assert call(B=12) == UNSUP
     assert call(Hq=6, Hkv=2) == UNSUP        # group 3
     assert call(q=24) == UNSUP               # misaligned
+    assert call(scale=0.0) == UNSUP
+    assert call(scale=-0.5) == UNSUP
+    assert call(scale=float("nan")) == UNSUP
     assert call(T=0, out=None, q=None) == OK  # nothing to do
     assert call(Lmax=0, out=None) == OK

@@ -5,6 +5,8 @@
 """
 
 import json
+
+import numpy as np
 import os
 
 from paged_kv_cache_362_amd import sizing
@@ -91,3 +93,10 @@ def test_internal_fragmentation():
     assert sizing.internal_fragmentation([64, 32], 32) == 0.0
     assert sizing.internal_fragmentation([1], 8) == 7 / 8
     assert sizing.internal_fragmentation([], 16) == 0.0
+
+
+def test_prefill_flops_match_the_oracle_count():
+    import oracle.paged_attention as O
+    for lens, chunks in [([8192], [8192]), ([8192], [2048]), ([5, 40, 9], [5, 3, 0])]:
+        qsl = np.concatenate([[0], np.cumsum(chunks)])
+        assert sizing.prefill_flops(lens, chunks, 32, 64) == O.prefill_flops(lens, qsl, 32, 64)
