@@ -147,28 +147,32 @@ __device__ __forceinline__ float group_sum(float v) {
 // chunks of one key tile, held in registers by every thread.
 template <int D> struct KVStage {
   using S = PfShape<D, 2>;
-  int kphys[S::KCH_T], vphys[S::VIT_T];
+  uint32_t kphys[S::KCH_T], vphys[S::VIT_T];
   u32x4 k[S::KCH_T], v0[S::VIT_T], v1[S::VIT_T];
 };
 
-// What each thread stages of a key tile, and how.
+// What each thread stages of a key tile, and how. Global addresses are one
+// unsigned 32 x 32 -> 64-bit multiply-add per block plus a 32-bit in-block
+// offset; LDS offsets are fixed per thread.
 template <int D> struct Stager {
   using S = PfShape<D, 2>;
   const char *kbase;     // k_cache + kh * B * D elements, in bytes
   const char *vbase;
   const int32_t *table;  // this sequence's table row
-  int64_t blk_bytes;     // Hkv * B * D * 2: one physical block of all KV heads
-  int bshift, bmask;
-  int n;                 // context length
-  int kkey[S::KCH_T], kdc[S::KCH_T];   // K chunks of this thread
-  int vkey[S::VIT_T], vdc[S::VIT_T];   // V (even key, chunk) items of this thread
+  uint32_t blk_bytes;    // Hkv * B * D * 2: one physical block of all KV heads
+  uint32_t bshift, bmask;
+  uint32_t last_pos;     // context length - 1
+  uint32_t kkey[S::KCH_T], kcol[S::KCH_T];  // K chunks of this thread: key, byte column
+  uint32_t vkey[S::VIT_T], vcol[S::VIT_T];  // V (even key, byte column) items
+  uint32_t klds[S::KCH_T], vlds[S::VIT_T];  // their LDS byte offsets in a stage
 
   __device__ void init(int tid) {
 #pragma unroll
     for (int u = 0; u < S::KCH_T; ++u) {
       const int c = tid + u * kPfThreads;
       kkey[u] = c / S::DCH;
-      kdc[u] = c % S::DCH;
+      kcol[u] = (c % S::DCH) * 16;
+      klds[u] = kkey[u] * S::KPITCH + kcol[u];
     }
 #pragma unroll
     for (int u = 0; u < S::VIT_T; ++u) {
@@ -176,50 +180,51 @@ template <int D> struct Stager {
       // lower ones' items (identical loads and LDS writes), so no branch.
       const int it = (tid + u * kPfThreads) % S::VITEMS;
       vkey[u] = 2 * (it % (kTileKeys / 2));
-      vdc[u] = it / (kTileKeys / 2);
+      const int dc = it / (kTileKeys / 2);
+      vcol[u] = dc * 16;
+      vlds[u] = S::KBYTES + v_slot(vkey[u]) * 2 + 8 * dc * S::VPITCH;
     }
   }
   // Position of key `key` of tile j, clamped to the last cached position: keys
   // past the context read real data that the softmax then gives weight 0.
-  __device__ __forceinline__ int pos_of(int j, int key) const { return min(j * kTileKeys + key, n - 1); }
+  __device__ __forceinline__ uint32_t pos_of(int j, uint32_t key) const {
+    return min(uint32_t(j) * kTileKeys + key, last_pos);
+  }
+  __device__ __forceinline__ const char *row(const char *base, uint32_t phys, uint32_t pos) const {
+    return base + (uint64_t(phys) * blk_bytes + ((pos & bmask) * (D * 2)));
+  }
 
   __device__ void load_table(KVStage<D> &r, int j) const {
 #pragma unroll
-    for (int u = 0; u < S::KCH_T; ++u) r.kphys[u] = table[pos_of(j, kkey[u]) >> bshift];
+    for (int u = 0; u < S::KCH_T; ++u) r.kphys[u] = uint32_t(table[pos_of(j, kkey[u]) >> bshift]);
 #pragma unroll
-    for (int u = 0; u < S::VIT_T; ++u) r.vphys[u] = table[pos_of(j, vkey[u]) >> bshift];
+    for (int u = 0; u < S::VIT_T; ++u) r.vphys[u] = uint32_t(table[pos_of(j, vkey[u]) >> bshift]);
   }
   __device__ void load_kv(KVStage<D> &r, int j) const {
 #pragma unroll
-    for (int u = 0; u < S::KCH_T; ++u) {
-      const int pos = pos_of(j, kkey[u]);
-      const int64_t off = int64_t(r.kphys[u]) * blk_bytes + (pos & bmask) * (D * 2) + kdc[u] * 16;
-      r.k[u] = *reinterpret_cast<const u32x4 *>(kbase + off);
-    }
+    for (int u = 0; u < S::KCH_T; ++u)
+      r.k[u] = *reinterpret_cast<const u32x4 *>(row(kbase, r.kphys[u], pos_of(j, kkey[u])) + kcol[u]);
 #pragma unroll
     for (int u = 0; u < S::VIT_T; ++u) {
       // The two keys of a pair are in one block (even key, block size >= 8).
-      const int p0 = pos_of(j, vkey[u]), p1 = pos_of(j, vkey[u] + 1);
-      const int64_t b = int64_t(r.vphys[u]) * blk_bytes + vdc[u] * 16;
-      r.v0[u] = *reinterpret_cast<const u32x4 *>(vbase + b + (p0 & bmask) * (D * 2));
-      r.v1[u] = *reinterpret_cast<const u32x4 *>(vbase + b + (p1 & bmask) * (D * 2));
+      r.v0[u] = *reinterpret_cast<const u32x4 *>(row(vbase, r.vphys[u], pos_of(j, vkey[u])) + vcol[u]);
+      r.v1[u] = *reinterpret_cast<const u32x4 *>(row(vbase, r.vphys[u], pos_of(j, vkey[u] + 1)) + vcol[u]);
     }
   }
   __device__ void store_lds(const KVStage<D> &r, char *buf) const {
 #pragma unroll
-    for (int u = 0; u < S::KCH_T; ++u)
-      *reinterpret_cast<u32x4 *>(buf + kkey[u] * S::KPITCH + kdc[u] * 16) = r.k[u];
+    for (int u = 0; u < S::KCH_T; ++u) *reinterpret_cast<u32x4 *>(buf + klds[u]) = r.k[u];
 #pragma unroll
     for (int u = 0; u < S::VIT_T; ++u) {
-      char *col = buf + S::KBYTES + v_slot(vkey[u]) * 2;
+      char *col = buf + vlds[u];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t a = r.v0[u][w], b = r.v1[u][w];
         // dims 8*dc + 2w and 8*dc + 2w + 1: (key, key + 1) pairs of each
         const uint32_t even = __builtin_amdgcn_perm(b, a, 0x05040100u);
         const uint32_t odd = __builtin_amdgcn_perm(b, a, 0x07060302u);
-        *reinterpret_cast<uint32_t *>(col + (8 * vdc[u] + 2 * w) * S::VPITCH) = even;
-        *reinterpret_cast<uint32_t *>(col + (8 * vdc[u] + 2 * w + 1) * S::VPITCH) = odd;
+        *reinterpret_cast<uint32_t *>(col + (2 * w) * S::VPITCH) = even;
+        *reinterpret_cast<uint32_t *>(col + (2 * w + 1) * S::VPITCH) = odd;
       }
     }
   }
@@ -277,10 +282,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams p) {
   st.kbase = reinterpret_cast<const char *>(p.k_cache) + int64_t(kh) * p.block_size * D * 2;
   st.vbase = reinterpret_cast<const char *>(p.v_cache) + int64_t(kh) * p.block_size * D * 2;
   st.table = p.block_tables + int64_t(seq) * p.max_blocks_per_seq;
-  st.blk_bytes = int64_t(p.num_kv_heads) * p.block_size * D * 2;
+  st.blk_bytes = uint32_t(p.num_kv_heads) * p.block_size * D * 2;
   st.bshift = p.block_shift;
   st.bmask = p.block_size - 1;
-  st.n = n;
+  st.last_pos = n - 1;
   st.init(tid);
 
   f32x4 acc[QB][S::DB];
@@ -293,10 +298,10 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams p) {
     for (int db = 0; db < S::DB; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Pipeline of NSET register stages: at the top of iteration j, stage
-  // (j + i) % NSET holds the loads in flight for tile j + i (0 < i < NSET),
-  // stage j % NSET is free and holds the table entries of tile j + NSET, and
-  // LDS buffer j & 1 holds tile j. Tiles past the last are clamped to it, and
+  // Pipeline of NSET register stages and NSET LDS buffers: at the top of
+  // iteration j, stage (j + i) % NSET holds the loads in flight for tile j + i
+  // (0 < i < NSET), stage j % NSET is free and holds the table entries of tile
+  // j + NSET, and LDS buffer j % NSET holds tile j. Tiles past the last are clamped to it, and
   // iterations past it compute with every key masked (no effect), so the loop
   // runs a multiple of NSET iterations with compile-time stage indices.
   const int last = ntiles - 1;
@@ -318,7 +323,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams p) {
       st.load_kv(mine, min(j + NSET, last));
       st.load_table(next, min(j + NSET + 1, last));
       const bool live = j < ntiles;
-      const char *kb_lds = lds + (j & 1) * S::BUF;
+      const char *kb_lds = lds + u * S::BUF;
       const char *vt_lds = kb_lds + S::KBYTES;
 
       // S^T = K . Q^T for 2 blocks of 16 keys.
@@ -406,7 +411,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams p) {
         }
       }
 
-      st.store_lds(next, lds + ((j + 1) & 1) * S::BUF);
+      st.store_lds(next, lds + ((u + 1) % NSET) * S::BUF);
       __syncthreads();
     }
   }
@@ -434,13 +439,13 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams p) {
 template <int DT, int D, int G>
 hipError_t launch_g(const PrefillParams &p, hipStream_t stream) {
   constexpr int QB = 2;
-  constexpr int NSET = D == 64 ? 3 : 2;
+  constexpr int NSET = 2;
   using S = PfShape<D, QB>;
   const int64_t items = int64_t(p.num_seqs) * p.num_kv_heads * p.q_tiles;
   if (items == 0) return hipSuccess;
   const int64_t grid = (items + 7) / 8 * 8;
   hipLaunchKernelGGL((prefill_kernel<DT, D, G, QB, NSET>), dim3(unsigned(grid)), dim3(kPfThreads),
-                     2 * S::BUF, stream, p);
+                     NSET * S::BUF, stream, p);
   return hipGetLastError();
 }
 
