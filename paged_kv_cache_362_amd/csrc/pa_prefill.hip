@@ -27,8 +27,8 @@
 // Computing the transposed scores puts each query row in one lane column, so
 // the softmax weights P^T feed the second product from the registers they are
 // in. The online softmax runs in the log2 domain with a running maximum per
-// row that is raised lazily (see kRescaleSlack); the row sum is kept per lane
-// and reduced once at the end. Scores are masked only in the tiles that cross
+// row that is raised lazily (see kRescaleSlack); the row sums come from one
+// more MFMA per row block against an all-ones V^T block. Scores are masked only in the tiles that cross
 // a row's position. The scale must be positive (the tile maximum is taken on
 // unscaled scores).
 //
@@ -110,7 +110,7 @@ template <> __device__ __forceinline__ float unpack_hi<PA_BF16>(uint32_t w) {
   return __builtin_bit_cast(float, w & 0xffff0000u);
 }
 
-// Maximum / sum over the 4 lanes l, l^16, l^32, l^48 (the lane groups that
+// Maximum over the 4 lanes l, l^16, l^32, l^48 (the lane groups that
 // hold one query row's keys). permlane16_swap hands each lane the values of
 // its row pair (rows 2r, 2r+1), permlane32_swap those of lanes l%32 and
 // 32 + l%32: two VALU exchanges, no LDS traffic. The pair's elements are
@@ -135,12 +135,6 @@ __device__ __forceinline__ float group_max(float v) {
   swap16(v, a, b);
   swap32(fmaxf(a, b), a, b);
   return fmaxf(a, b);
-}
-__device__ __forceinline__ float group_sum(float v) {
-  float a, b;
-  swap16(v, a, b);
-  swap32(a + b, a, b);
-  return a + b;
 }
 
 // One stage of the global -> LDS pipeline: the table entries and the K/V
@@ -288,15 +282,20 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams p) {
   st.last_pos = n - 1;
   st.init(tid);
 
-  f32x4 acc[QB][S::DB];
-  float m[QB], l[QB];
+  // acc: O^T blocks; lsum: the row sums of P, as one more O^T block whose
+  // V^T rows are all ones (the MFMA sums the weights it is given, so the
+  // denominator uses exactly the rounded weights the numerator does).
+  f32x4 acc[QB][S::DB], lsum[QB];
+  float m[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m[qb] = -INFINITY;
-    l[qb] = 0.f;
+    lsum[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < S::DB; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const uint32_t one2 = DT == PA_F16 ? 0x3C003C00u : 0x3F803F80u;  // two 1.0 elements
+  const u32x4 ones = {one2, one2, one2, one2};
 
   // Pipeline of NSET register stages and NSET LDS buffers: at the top of
   // iteration j, stage (j + i) % NSET holds the loads in flight for tile j + i
@@ -376,7 +375,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams p) {
           const float m_new = fmaxf(m[qb], tmax[qb]);
           const float alpha = fast_exp2(m[qb] - m_new);
           m[qb] = m_new;
-          l[qb] *= alpha;
+          lsum[qb] *= alpha;
 #pragma unroll
           for (int db = 0; db < S::DB; ++db) acc[qb][db] *= alpha;
         }
@@ -390,7 +389,6 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
             e[4 * kb + jj] = fast_exp2(fmaf(s[qb][kb][jj], p.scale_log2, -m[qb]));
-        l[qb] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const uint32_t hw = cvt2<DT>(e[2 * w], e[2 * w + 1]);
@@ -400,7 +398,12 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams p) {
         }
       }
 
-      // O^T += V^T . P^T
+      // O^T += V^T . P^T, and the row sums.
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        lsum[qb] = mfma16<DT>(ones, ph[qb], lsum[qb]);
+        if (DT == PA_BF16) lsum[qb] = mfma16<DT>(ones, pl[qb], lsum[qb]);
+      }
 #pragma unroll
       for (int db = 0; db < S::DB; ++db) {
         const u32x4 a = *reinterpret_cast<const u32x4 *>(vt_lds + (16 * db + lr) * S::VPITCH + 16 * lg);
@@ -419,7 +422,7 @@ __global__ __launch_bounds__(kPfThreads) void prefill_kernel(PrefillParams p) {
   // out = acc / l for the valid rows.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float inv = 1.f / group_sum(l[qb]);
+    const float inv = 1.f / lsum[qb][0];
     const int r = qt * S::ROWS + (wave * QB + qb) * 16 + lr;
     const int t = r / G;
     if (t >= L) continue;
