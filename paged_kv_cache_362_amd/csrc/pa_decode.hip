@@ -375,6 +375,17 @@ __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int 
     c.voff = (lane / S::LPT) * S::ROWB + (lane % S::LPT) * 16;
   }
 
+  const int seg_tiles = (p_end - p_start + 15) >> 4;
+  constexpr int kWin = kWaves * chunk_tiles<BS8>();
+  // The table entries of this wave's part of the first window are requested
+  // before the query rows are staged, so the two loads overlap.
+  int tab_first;
+  {
+    const int win = min(kWin, seg_tiles);
+    const int tok0 = p_start + 16 * (wave * win / kWaves);
+    tab_first = table_row[min((tok0 >> c.bshift) + lane, p.max_blocks_per_seq - 1)];
+  }
+
   // MFMA operand B (lane l: query head (l % 16) % G, chunk (l / 16) + 4 s) is
   // read from LDS: the group's query rows are staged there once per segment.
   {
@@ -406,8 +417,6 @@ __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int 
       for (int e = 0; e < S::EPC; ++e) st.acc[h][sg][e] = 0.0f;
 
   const float sl2 = p.scale_log2;
-  const int seg_tiles = (p_end - p_start + 15) >> 4;
-  constexpr int kWin = kWaves * chunk_tiles<BS8>();
   for (int w0 = 0; w0 < seg_tiles; w0 += kWin) {
     const int win = min(kWin, seg_tiles - w0);
     const int t0 = w0 + wave * win / kWaves;
@@ -417,8 +426,9 @@ __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int 
     const int tok_end = min(p_start + 16 * t1, p_end);
     c.first_blk = tok0 >> c.bshift;
     {
-      const int idx = min(c.first_blk + lane, p.max_blocks_per_seq - 1);
-      c.tabv = min(max(table_row[idx], 0), p.num_blocks - 1);  // never address outside the pool
+      int raw = tab_first;
+      if (w0 > 0) raw = table_row[min(c.first_blk + lane, p.max_blocks_per_seq - 1)];
+      c.tabv = min(max(raw, 0), p.num_blocks - 1);  // never address outside the pool
     }
     const int nr = (t1 - t0 + NT - 1) / NT;
     auto rtok_of = [&](int r) { return tok0 + r * S::ROUND; };
