@@ -654,8 +654,11 @@ __device__ __forceinline__ void copy_new_rows(const DecodeParams &p, int first) 
   }
 }
 
-template <int DT, int D, int G, int NT, bool BS8, bool STEP>
-__global__ __launch_bounds__(kThreads) void decode_flat_kernel(DecodeParams p) {
+// MIN_WAVES: the minimum waves per SIMD the register allocation must allow
+// (1: no constraint).
+template <int DT, int D, int G, int NT, bool BS8, bool STEP, int MIN_WAVES>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MIN_WAVES)))
+void decode_flat_kernel(DecodeParams p) {
   using OutT = typename Store<DT>::T;
   extern __shared__ int s_plan[];  // tiles prefix [S + 1], clamped lengths [S], slots [S]
   __shared__ MergeLds<G, D> lds;
@@ -840,7 +843,12 @@ template <int DT, int D, int G> constexpr int rounds_tiles() {
 template <int DT, int D, int G, bool BS8, bool STEP>
 static hipError_t launch_flat(const DecodeParams &p, hipStream_t stream) {
   constexpr int NT = rounds_tiles<DT, D, G>();
-  auto kern = decode_flat_kernel<DT, D, G, NT, BS8, STEP>;
+  // The fp16/bf16 fused-step instances with 4 query heads per KV head at
+  // head_dim 128 would otherwise allocate ~170-210 VGPRs (2 waves per SIMD);
+  // bounded to 168 they need no scratch and keep 3 waves of K/V loads in
+  // flight. (fp32 would spill.)
+  constexpr int kMinWaves = (STEP && DT != PA_F32 && D == 128 && G == 4) ? 3 : 1;
+  auto kern = decode_flat_kernel<DT, D, G, NT, BS8, STEP, kMinWaves>;
   const size_t shmem = flat_plan_lds_bytes(p.num_seqs);
   const int64_t max_tiles =
       (int64_t)p.num_seqs * p.num_kv_heads * ((p.max_context_len + 15) / 16);
