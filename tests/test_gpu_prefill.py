@@ -41,6 +41,8 @@ CASES = [
     ("f16", 4, 2, 64, 64, [500, 3], [200, 3]),            # 64-token blocks
     ("bf16", 2, 2, 128, 16, [161, 90, 33], [0, 90, 33]),  # an empty chunk
     ("f16", 8, 4, 128, 16, [1, 2, 31, 32, 33], [1, 2, 31, 32, 33]),  # tile edges
+    ("bf16", 16, 2, 128, 16, [140, 77], [139, 77]),      # GQA 8 at D 128
+    ("f16", 2, 1, 64, 16, [1000], [260]),                # long prefix, 3 row tiles
 ]
 
 
