@@ -56,9 +56,7 @@ template <int D, int QB> struct PfShape {
   static constexpr int KBYTES = kTileKeys * KPITCH;
   static constexpr int BUF = KBYTES + D * VPITCH;        // one stage
   static constexpr int DCH = D / 8;                      // 16-byte chunks per row
-  static constexpr int KCH_T = kTileKeys * DCH / kPfThreads;        // K chunks per thread
-  static constexpr int VITEMS = (kTileKeys / 2) * DCH;              // (key pair, chunk) items
-  static constexpr int VIT_T = (VITEMS + kPfThreads - 1) / kPfThreads;
+  static constexpr int KCH_T = kTileKeys * DCH / kPfThreads;        // (key, column) items per thread
   static_assert(kTileKeys * DCH % kPfThreads == 0, "K chunks must divide over the threads");
   static_assert(ROWS == kPrefillRows, "tile rows and host constant disagree");
 };
@@ -141,13 +139,22 @@ __device__ __forceinline__ float group_max(float v) {
 // chunks of one key tile, held in registers by every thread.
 template <int D> struct KVStage {
   using S = PfShape<D, 2>;
-  uint32_t kphys[S::KCH_T], vphys[S::VIT_T];
-  u32x4 k[S::KCH_T], v0[S::VIT_T], v1[S::VIT_T];
+  uint32_t phys[S::KCH_T];
+  u32x4 k[S::KCH_T], v[S::KCH_T];
 };
 
-// What each thread stages of a key tile, and how. Global addresses are one
-// unsigned 32 x 32 -> 64-bit multiply-add per block plus a 32-bit in-block
-// offset; LDS offsets are fixed per thread.
+// Value of v in lane l ^ 1 (DPP quad_perm [1, 0, 3, 2]).
+__device__ __forceinline__ uint32_t lane_pair(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0xB1, 0xF, 0xF, false));
+}
+
+// What each thread stages of a key tile, and how. Thread item p (p = tid +
+// 256 u) is key p % 32, 16-byte column p / 32, of both K and V: one table
+// entry and one address per item. Keys vary fastest across lanes, so the
+// transposed V stores of a wave spread over the LDS banks, and the two keys of
+// an (even, odd) pair sit in lanes l and l ^ 1; for the transposed V tile they
+// swap two dwords so that each lane writes 4 of the pair's 8 (key, key+1)
+// dwords.
 template <int D> struct Stager {
   using S = PfShape<D, 2>;
   const char *kbase;     // k_cache + kh * B * D elements, in bytes
@@ -156,70 +163,57 @@ template <int D> struct Stager {
   uint32_t blk_bytes;    // Hkv * B * D * 2: one physical block of all KV heads
   uint32_t bshift, bmask;
   uint32_t last_pos;     // context length - 1
-  uint32_t kkey[S::KCH_T], kcol[S::KCH_T];  // K chunks of this thread: key, byte column
-  uint32_t vkey[S::VIT_T], vcol[S::VIT_T];  // V (even key, byte column) items
-  uint32_t klds[S::KCH_T], vlds[S::VIT_T];  // their LDS byte offsets in a stage
+  uint32_t key[S::KCH_T], col[S::KCH_T];  // item's key in the tile and byte column
+  uint32_t klds[S::KCH_T], vlds[S::KCH_T];
+  bool odd[S::KCH_T];
 
   __device__ void init(int tid) {
 #pragma unroll
     for (int u = 0; u < S::KCH_T; ++u) {
-      const int c = tid + u * kPfThreads;
-      kkey[u] = c / S::DCH;
-      kcol[u] = (c % S::DCH) * 16;
-      klds[u] = kkey[u] * S::KPITCH + kcol[u];
-    }
-#pragma unroll
-    for (int u = 0; u < S::VIT_T; ++u) {
-      // D = 64 has fewer items than threads: the upper threads repeat the
-      // lower ones' items (identical loads and LDS writes), so no branch.
-      const int it = (tid + u * kPfThreads) % S::VITEMS;
-      vkey[u] = 2 * (it % (kTileKeys / 2));
-      const int dc = it / (kTileKeys / 2);
-      vcol[u] = dc * 16;
-      vlds[u] = S::KBYTES + v_slot(vkey[u]) * 2 + 8 * dc * S::VPITCH;
+      const int p = tid + u * kPfThreads;
+      key[u] = p % kTileKeys;
+      const int c = p / kTileKeys;
+      col[u] = c * 16;
+      klds[u] = key[u] * S::KPITCH + col[u];
+      odd[u] = key[u] & 1;
+      vlds[u] = S::KBYTES + v_slot(key[u] & ~1u) * 2 + (8 * c + 4 * (key[u] & 1)) * S::VPITCH;
     }
   }
-  // Position of key `key` of tile j, clamped to the last cached position: keys
+  // Position of key `k` of tile j, clamped to the last cached position: keys
   // past the context read real data that the softmax then gives weight 0.
-  __device__ __forceinline__ uint32_t pos_of(int j, uint32_t key) const {
-    return min(uint32_t(j) * kTileKeys + key, last_pos);
-  }
-  __device__ __forceinline__ const char *row(const char *base, uint32_t phys, uint32_t pos) const {
-    return base + (uint64_t(phys) * blk_bytes + ((pos & bmask) * (D * 2)));
+  __device__ __forceinline__ uint32_t pos_of(int j, uint32_t k) const {
+    return min(uint32_t(j) * kTileKeys + k, last_pos);
   }
 
   __device__ void load_table(KVStage<D> &r, int j) const {
 #pragma unroll
-    for (int u = 0; u < S::KCH_T; ++u) r.kphys[u] = uint32_t(table[pos_of(j, kkey[u]) >> bshift]);
-#pragma unroll
-    for (int u = 0; u < S::VIT_T; ++u) r.vphys[u] = uint32_t(table[pos_of(j, vkey[u]) >> bshift]);
+    for (int u = 0; u < S::KCH_T; ++u) r.phys[u] = uint32_t(table[pos_of(j, key[u]) >> bshift]);
   }
   __device__ void load_kv(KVStage<D> &r, int j) const {
 #pragma unroll
-    for (int u = 0; u < S::KCH_T; ++u)
-      r.k[u] = *reinterpret_cast<const u32x4 *>(row(kbase, r.kphys[u], pos_of(j, kkey[u])) + kcol[u]);
-#pragma unroll
-    for (int u = 0; u < S::VIT_T; ++u) {
-      // The two keys of a pair are in one block (even key, block size >= 8).
-      r.v0[u] = *reinterpret_cast<const u32x4 *>(row(vbase, r.vphys[u], pos_of(j, vkey[u])) + vcol[u]);
-      r.v1[u] = *reinterpret_cast<const u32x4 *>(row(vbase, r.vphys[u], pos_of(j, vkey[u] + 1)) + vcol[u]);
+    for (int u = 0; u < S::KCH_T; ++u) {
+      const uint64_t off = uint64_t(r.phys[u]) * blk_bytes + ((pos_of(j, key[u]) & bmask) * (D * 2) + col[u]);
+      r.k[u] = *reinterpret_cast<const u32x4 *>(kbase + off);
+      r.v[u] = *reinterpret_cast<const u32x4 *>(vbase + off);
     }
   }
   __device__ void store_lds(const KVStage<D> &r, char *buf) const {
 #pragma unroll
-    for (int u = 0; u < S::KCH_T; ++u) *reinterpret_cast<u32x4 *>(buf + klds[u]) = r.k[u];
-#pragma unroll
-    for (int u = 0; u < S::VIT_T; ++u) {
-      char *col = buf + vlds[u];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a = r.v0[u][w], b = r.v1[u][w];
-        // dims 8*dc + 2w and 8*dc + 2w + 1: (key, key + 1) pairs of each
-        const uint32_t even = __builtin_amdgcn_perm(b, a, 0x05040100u);
-        const uint32_t odd = __builtin_amdgcn_perm(b, a, 0x07060302u);
-        *reinterpret_cast<uint32_t *>(col + (2 * w) * S::VPITCH) = even;
-        *reinterpret_cast<uint32_t *>(col + (2 * w + 1) * S::VPITCH) = odd;
-      }
+    for (int u = 0; u < S::KCH_T; ++u) {
+      *reinterpret_cast<u32x4 *>(buf + klds[u]) = r.k[u];
+      // Even key: keeps dims 0-3 of the column (own words 0, 1) and receives
+      // the odd key's; odd key: keeps dims 4-7 (own words 2, 3), receives the
+      // even key's.
+      const uint32_t o0 = r.v[u][0], o1 = r.v[u][1], o2 = r.v[u][2], o3 = r.v[u][3];
+      const uint32_t r0 = lane_pair(odd[u] ? o0 : o2);
+      const uint32_t r1 = lane_pair(odd[u] ? o1 : o3);
+      const uint32_t lo0 = odd[u] ? r0 : o0, lo1 = odd[u] ? r1 : o1;  // the even key's words
+      const uint32_t hi0 = odd[u] ? o2 : r0, hi1 = odd[u] ? o3 : r1;  // the odd key's words
+      char *dst = buf + vlds[u];
+      *reinterpret_cast<uint32_t *>(dst) = __builtin_amdgcn_perm(hi0, lo0, 0x05040100u);
+      *reinterpret_cast<uint32_t *>(dst + S::VPITCH) = __builtin_amdgcn_perm(hi0, lo0, 0x07060302u);
+      *reinterpret_cast<uint32_t *>(dst + 2 * S::VPITCH) = __builtin_amdgcn_perm(hi1, lo1, 0x05040100u);
+      *reinterpret_cast<uint32_t *>(dst + 3 * S::VPITCH) = __builtin_amdgcn_perm(hi1, lo1, 0x07060302u);
     }
   }
 };
