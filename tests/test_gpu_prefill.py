@@ -124,3 +124,27 @@ def test_prefill_checks_in_debug_mode(monkeypatch):
     ops.prefill(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
                 t["query_start_loc"], b.scale, b.max_query_len)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_prefill_random_shapes(seed):
+    """Seeded random mixes: dtype, head_dim, group, block size, and per
+    sequence a context length and a chunk length (0 .. context), every
+    output compared with the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    dtype = ["f16", "bf16"][seed % 2]
+    d = [64, 128][(seed // 2) % 2]
+    hkv = int(rng.integers(1, 4))
+    g = int(rng.choice([1, 2, 4, 8]))
+    bs = int(rng.choice([8, 16, 32, 64]))
+    s = int(rng.integers(1, 5))
+    lens = rng.integers(1, 420, size=s)
+    chunks = np.array([int(rng.integers(0, n + 1)) for n in lens])
+    if chunks.sum() == 0:
+        chunks[0] = lens[0]
+    b = layouts.make_prefill_batch(num_q_heads=hkv * g, num_kv_heads=hkv, head_dim=d, dtype=dtype,
+                                   block_size=bs, context_lens=lens, chunk_lens=chunks,
+                                   seed=seed, poison=True)
+    got = _run(b)
+    assert_decode_close(got, _oracle(b), dtype,
+                        f"seed {seed}: {dtype} D{d} Hkv{hkv} G{g} B{bs} lens {lens} chunks {chunks}")
