@@ -44,7 +44,9 @@
 //   of its own head (n % G) and the other heads' weights arrive by DPP/swizzle
 //   from the lanes of the same token group.
 // * Online softmax in the log2 domain, per (token group, head): each token
-//   group keeps its own running maximum, so the loop has no cross-lane max.
+//   group keeps its own reference maximum, so the loop has no cross-lane max,
+//   and raises it (rescaling the accumulators) only when a round exceeds it by
+//   2^8, so the per-round rescale is a rarely taken branch.
 // * Masking by select: scores of tokens at or past the context end are -inf and
 //   their V values are replaced by 0, so NaN in unused slots cannot leak. Table
 //   entries are clamped into [0, num_blocks), so no load leaves the pool.
@@ -279,33 +281,41 @@ __device__ __forceinline__ void consume_round(const RoundBuf<DT, D, G, NT> &R,
     }
   }
 
+  // Lazy rescale: the reference maximum st.m is raised only when some lane's
+  // round maximum exceeds it by more than 2^8 (log2 domain), a wave-uniform
+  // branch that is rarely taken after the first round. Weights are then at
+  // most 2^8, and the sums and accumulators stay relative to one reference,
+  // so the result is the same softmax; the usual every-round rescale of the
+  // accumulators is skipped.
   float mx = x[0][0];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < S::VI; ++i) mx = fmaxf(mx, x[t][i]);
-  const float m_new = fmaxf(st.m, mx);
-  const float m_safe = m_new == -INFINITY ? 0.0f : m_new;
-  const float alpha = fast_exp2(st.m - m_safe);
-  st.m = m_new;
+  if (__builtin_amdgcn_ballot_w64(mx > st.m + 8.0f) != 0) {
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = st.m == -INFINITY ? 0.0f : fast_exp2(st.m - m_new);
+    st.m = m_new;
+    st.l *= alpha;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float ah = from_head<G>(alpha, h);
+#pragma unroll
+      for (int sg = 0; sg < S::NSEG; ++sg)
+#pragma unroll
+        for (int e = 0; e < S::EPC; ++e) st.acc[h][sg][e] *= ah;
+    }
+  }
+  const float m_ref = st.m == -INFINITY ? 0.0f : st.m;
   float psum = 0.0f;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < S::VI; ++i) {
-      x[t][i] = fast_exp2(x[t][i] - m_safe);
+      x[t][i] = fast_exp2(x[t][i] - m_ref);
       psum += x[t][i];
     }
-  st.l = fmaf(st.l, alpha, psum);
-
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float ah = from_head<G>(alpha, h);
-#pragma unroll
-    for (int sg = 0; sg < S::NSEG; ++sg)
-#pragma unroll
-      for (int e = 0; e < S::EPC; ++e) st.acc[h][sg][e] *= ah;
-  }
+  st.l += psum;
 
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -346,6 +356,91 @@ template <int G, int D> struct MergeLds {
 // Tiles of a wave's chunk inside one window: at most 64 blocks of table.
 template <bool BS8> constexpr int chunk_tiles() { return BS8 ? 32 : 63; }
 
+// Per-lane K/V addressing constants of one KV head.
+template <int DT, int D, int G, int NT>
+__device__ __forceinline__ WaveCtx make_wave_ctx(const DecodeParams &p, int kh) {
+  using S = DecodeShape<DT, D, G, NT>;
+  const int lane = __lane_id();
+  WaveCtx c;
+  c.k_cache = reinterpret_cast<const char *>(p.k_cache);
+  c.v_cache = reinterpret_cast<const char *>(p.v_cache);
+  c.bshift = p.block_shift;
+  c.blk_bytes = (int64_t)p.num_kv_heads * (S::ROWB << c.bshift);
+  c.head_off = (int64_t)kh * (S::ROWB << c.bshift);
+  const int ktok = tile_token_of_row<S::LPT>(lane & 15);
+  c.koff = ktok * S::ROWB + (lane >> 4) * 16;
+  c.koff8 = (ktok & 7) * S::ROWB + (lane >> 4) * 16;
+  c.khi = ktok >= 8;
+  c.voff = (lane / S::LPT) * S::ROWB + (lane % S::LPT) * 16;
+  return c;
+}
+
+// The nr rounds of one chunk [tok0, tok_end) of a wave (its table entries are
+// in c.tabv), through two register buffers: at the top of the loop only A
+// (round r) is in flight.
+template <bool BS8, int DT, int D, int G, int NT>
+__device__ __forceinline__ void stream_rounds(const WaveCtx &c, SoftState<DT, D, G, NT> &st,
+                                              const u32x4 (*qb)[D * 4 / 16], const NewRow &new_row,
+                                              float sl2, int tok0, int tok_end, int nr) {
+  using S = DecodeShape<DT, D, G, NT>;
+  auto rtok_of = [&](int r) { return tok0 + r * S::ROUND; };
+  RoundBuf<DT, D, G, NT> A, B;
+  load_round<BS8>(A, c, rtok_of(0));
+  int r = 0;
+  while (r + 2 < nr) {
+    load_round<BS8>(B, c, rtok_of(r + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    consume_round<false>(A, st, qb, sl2, rtok_of(r), tok_end);
+    load_round<BS8>(A, c, rtok_of(r + 2));
+    __builtin_amdgcn_sched_barrier(0);
+    consume_round<false>(B, st, qb, sl2, rtok_of(r + 1), tok_end);
+    r += 2;
+  }
+  // Rounds r and (if it exists) r + 1 remain; only the chunk's last round can be partial.
+  if (r + 1 < nr) {
+    load_round<BS8>(B, c, rtok_of(r + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    consume_round<false>(A, st, qb, sl2, rtok_of(r), tok_end);
+    if (new_row.pos >= 0) apply_new_row(B, new_row, rtok_of(r + 1));
+    consume_round<true>(B, st, qb, sl2, rtok_of(r + 1), tok_end);
+  } else {
+    if (new_row.pos >= 0) apply_new_row(A, new_row, rtok_of(r));
+    consume_round<true>(A, st, qb, sl2, rtok_of(r), tok_end);
+  }
+}
+
+// Merge the token groups of the wave (lanes l, l ^ LPT, l ^ 2 LPT, ... hold the
+// same row chunk for different tokens). Afterwards every lane holds each
+// head's wave maximum mw and sum lw, and lanes l < LPT the head's merged
+// weighted sums of row chunk l (relative to mw) in st.acc.
+template <int DT, int D, int G, int NT>
+__device__ __forceinline__ void merge_token_groups(SoftState<DT, D, G, NT> &st, float (&mw)[G],
+                                                   float (&lw)[G]) {
+  using S = DecodeShape<DT, D, G, NT>;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float mg = from_head<G>(st.m, h);
+    float m = mg;
+#pragma unroll
+    for (int mask = S::LPT; mask < kWave; mask <<= 1) m = fmaxf(m, __shfl_xor(m, mask));
+    const float f = m == -INFINITY ? 0.0f : fast_exp2(mg - m);
+    float l = from_head<G>(st.l, h) * f;
+#pragma unroll
+    for (int mask = S::LPT; mask < kWave; mask <<= 1) l += __shfl_xor(l, mask);
+#pragma unroll
+    for (int sg = 0; sg < S::NSEG; ++sg)
+#pragma unroll
+      for (int e = 0; e < S::EPC; ++e) {
+        float a = st.acc[h][sg][e] * f;
+#pragma unroll
+        for (int mask = S::LPT; mask < kWave; mask <<= 1) a += __shfl_xor(a, mask);
+        st.acc[h][sg][e] = a;
+      }
+    mw[h] = m;
+    lw[h] = l;
+  }
+}
+
 // A segment [p_start, p_end) of sequence `seq`, KV head `kh`, processed by the
 // four waves. The segment is cut into windows of up to 4 * chunk_tiles tiles;
 // each wave takes a contiguous quarter of a window (a chunk that touches at
@@ -361,19 +456,7 @@ __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int 
   const int num_q_heads = p.num_kv_heads * G;
   const int32_t *table_row = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
 
-  WaveCtx c;
-  c.k_cache = reinterpret_cast<const char *>(p.k_cache);
-  c.v_cache = reinterpret_cast<const char *>(p.v_cache);
-  c.bshift = p.block_shift;
-  c.blk_bytes = (int64_t)p.num_kv_heads * (S::ROWB << c.bshift);
-  c.head_off = (int64_t)kh * (S::ROWB << c.bshift);
-  {
-    const int ktok = tile_token_of_row<S::LPT>(lane & 15);
-    c.koff = ktok * S::ROWB + (lane >> 4) * 16;
-    c.koff8 = (ktok & 7) * S::ROWB + (lane >> 4) * 16;
-    c.khi = ktok >= 8;
-    c.voff = (lane / S::LPT) * S::ROWB + (lane % S::LPT) * 16;
-  }
+  WaveCtx c = make_wave_ctx<DT, D, G, NT>(p, kh);
 
   const int seg_tiles = (p_end - p_start + 15) >> 4;
   constexpr int kWin = kWaves * chunk_tiles<BS8>();
@@ -430,56 +513,13 @@ __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int 
       if (w0 > 0) raw = table_row[min(c.first_blk + lane, p.max_blocks_per_seq - 1)];
       c.tabv = min(max(raw, 0), p.num_blocks - 1);  // never address outside the pool
     }
-    const int nr = (t1 - t0 + NT - 1) / NT;
-    auto rtok_of = [&](int r) { return tok0 + r * S::ROUND; };
-
-    // Two register buffers; at the top of the loop only A (round r) is in flight.
-    RoundBuf<DT, D, G, NT> A, B;
-    load_round<BS8>(A, c, rtok_of(0));
-    int r = 0;
-    while (r + 2 < nr) {
-      load_round<BS8>(B, c, rtok_of(r + 1));
-      __builtin_amdgcn_sched_barrier(0);
-      consume_round<false>(A, st, qb, sl2, rtok_of(r), tok_end);
-      load_round<BS8>(A, c, rtok_of(r + 2));
-      __builtin_amdgcn_sched_barrier(0);
-      consume_round<false>(B, st, qb, sl2, rtok_of(r + 1), tok_end);
-      r += 2;
-    }
-    // Rounds r and (if it exists) r + 1 remain; only the chunk's last round can be partial.
-    if (r + 1 < nr) {
-      load_round<BS8>(B, c, rtok_of(r + 1));
-      __builtin_amdgcn_sched_barrier(0);
-      consume_round<false>(A, st, qb, sl2, rtok_of(r), tok_end);
-      if (new_pos >= 0) apply_new_row(B, new_row, rtok_of(r + 1));
-      consume_round<true>(B, st, qb, sl2, rtok_of(r + 1), tok_end);
-    } else {
-      if (new_pos >= 0) apply_new_row(A, new_row, rtok_of(r));
-      consume_round<true>(A, st, qb, sl2, rtok_of(r), tok_end);
-    }
+    stream_rounds<BS8>(c, st, qb, new_row, sl2, tok0, tok_end, (t1 - t0 + NT - 1) / NT);
   }
 
-  // Merge the token groups of the wave (lanes l, l ^ LPT, l ^ 2 LPT, ... hold the
-  // same row chunk for different tokens).
+  float mw[G], lw[G];
+  merge_token_groups(st, mw, lw);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float mg = from_head<G>(st.m, h);
-    float mw = mg;
-#pragma unroll
-    for (int mask = S::LPT; mask < kWave; mask <<= 1) mw = fmaxf(mw, __shfl_xor(mw, mask));
-    const float f = mw == -INFINITY ? 0.0f : fast_exp2(mg - mw);
-    float lw = from_head<G>(st.l, h) * f;
-#pragma unroll
-    for (int mask = S::LPT; mask < kWave; mask <<= 1) lw += __shfl_xor(lw, mask);
-#pragma unroll
-    for (int sg = 0; sg < S::NSEG; ++sg)
-#pragma unroll
-      for (int e = 0; e < S::EPC; ++e) {
-        float a = st.acc[h][sg][e] * f;
-#pragma unroll
-        for (int mask = S::LPT; mask < kWave; mask <<= 1) a += __shfl_xor(a, mask);
-        st.acc[h][sg][e] = a;
-      }
     if (lane < S::LPT) {
 #pragma unroll
       for (int sg = 0; sg < S::NSEG; ++sg)
@@ -488,8 +528,8 @@ __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int 
           lds.acc[wave][h][sg * (S::SEGB / S::E) + lane * S::EPC + e] = st.acc[h][sg][e];
     }
     if (lane == 0) {
-      lds.m[wave][h] = mw;
-      lds.l[wave][h] = lw;
+      lds.m[wave][h] = mw[h];
+      lds.l[wave][h] = lw[h];
     }
   }
 }
@@ -840,14 +880,23 @@ template <int DT, int D, int G> constexpr int rounds_tiles() {
   return (D * Elem<DT>::kBytes) >= 256 ? 1 : 2;
 }
 
+// Register bound of the balanced-form instances (waves per SIMD the
+// allocation must allow). Where set, the instance fits with no scratch, while
+// unbounded the compiler takes a few registers more and loses a wave per SIMD:
+// 16-bit head_dim 128 with one query head per KV head fits 128 VGPRs (4 waves),
+// with two or four 168 (3 waves); fp16 head_dim 64 with one fits 128, 16-bit
+// head_dim 64 with two fits 168. Other instances would spill and stay unbounded.
+template <int DT, int D, int G> constexpr int flat_min_waves() {
+  if (DT == PA_F32) return 1;
+  if (D == 128) return G == 1 ? 4 : G <= 4 ? 3 : 1;
+  if (D == 64) return (G == 1 && DT == PA_F16) ? 4 : G == 2 ? 3 : 1;
+  return 1;
+}
+
 template <int DT, int D, int G, bool BS8, bool STEP>
 static hipError_t launch_flat(const DecodeParams &p, hipStream_t stream) {
   constexpr int NT = rounds_tiles<DT, D, G>();
-  // The fp16/bf16 fused-step instances with 4 query heads per KV head at
-  // head_dim 128 would otherwise allocate ~170-210 VGPRs (2 waves per SIMD);
-  // bounded to 168 they need no scratch and keep 3 waves of K/V loads in
-  // flight. (fp32 would spill.)
-  constexpr int kMinWaves = (STEP && DT != PA_F32 && D == 128 && G == 4) ? 3 : 1;
+  constexpr int kMinWaves = flat_min_waves<DT, D, G>();
   auto kern = decode_flat_kernel<DT, D, G, NT, BS8, STEP, kMinWaves>;
   const size_t shmem = flat_plan_lds_bytes(p.num_seqs);
   const int64_t max_tiles =
