@@ -193,6 +193,17 @@ int flat_grid_size(const void *kernel, int threads, size_t dynamic_lds, int64_t 
   return want < resident ? int(want) : resident;
 }
 
+// Tiles of work a segment's start and epilogue cost in the balanced plan;
+// PA_FLAT_SEG_COST overrides it (a tuning knob).
+int flat_segment_cost() {
+  static const int cost = [] {
+    int c = kFlatSegmentCost;
+    if (const char *e = std::getenv("PA_FLAT_SEG_COST")) c = std::atoi(e);
+    return c < 0 ? 0 : c > 1024 ? 1024 : c;
+  }();
+  return cost;
+}
+
 }  // namespace pa
 
 extern "C" {
@@ -539,6 +550,7 @@ int32_t decode_impl(void *out, const void *q, const void *k_cache, const void *v
   p.max_context_len = max_context_len;
   p.partition_size = balanced ? 0 : part;
   p.max_partitions = max_parts;
+  p.seg_cost = pa::flat_segment_cost();
   p.dtype = dtype;
   if (fused && balanced) {
     p.new_key = step.key;

@@ -721,8 +721,12 @@ void decode_flat_kernel(DecodeParams p) {
   NewRowCopy<DT, D, G> first_row;
   if (STEP) first_row.load(p, w);
 
-  // Plan: tiles per sequence and their prefix sums (every workgroup computes the
-  // same plan from context_lens).
+  // Plan: work units per sequence and their prefix sums (every workgroup
+  // computes the same plan from context_lens). A (sequence, KV head) of t tiles
+  // is `cost` units of overhead followed by its t tiles, so cutting the units
+  // evenly gives a workgroup whose range touches more (sequence, KV head)
+  // pairs fewer tiles: each segment costs a start-up and an epilogue.
+  const int cost = p.seg_cost;
   if (tid == 0) s_tc[0] = 0;
   int carry = 0;
   for (int base = 0; base < S; base += kThreads) {
@@ -730,6 +734,7 @@ void decode_flat_kernel(DecodeParams p) {
     int n = s < S ? min(p.context_lens[s], p.max_context_len) : 0;
     n = max(n, 0);
     int x = (n + 15) >> 4;
+    if (x > 0) x += cost;  // each (sequence, KV head) is charged `cost` tiles more
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
       const int y = __shfl_up(x, o);
@@ -781,12 +786,15 @@ void decode_flat_kernel(DecodeParams p) {
   int64_t pos = start;
   while (pos < end) {
     while (pos >= (int64_t)hkv * s_tc[seq + 1]) ++seq;  // skips empty sequences
-    const int tiles = s_tc[seq + 1] - s_tc[seq];
+    const int units = s_tc[seq + 1] - s_tc[seq];
+    const int tiles = units - cost;
     const int64_t seq_base = (int64_t)hkv * s_tc[seq];
-    const int kh = (int)((pos - seq_base) / tiles);
-    const int64_t item_base = seq_base + (int64_t)kh * tiles;
-    const int a = (int)(pos - item_base);
-    const int b = (int)min(end - item_base, (int64_t)tiles);
+    const int kh = (int)((pos - seq_base) / units);
+    const int64_t item_base = seq_base + (int64_t)kh * units;  // its overhead units, then its tiles
+    const int64_t tile_base = item_base + cost;
+    const int a = (int)max(pos - tile_base, (int64_t)0);
+    const int b = (int)min(end - tile_base, (int64_t)tiles);
+    if (b <= a) break;  // the range ends inside this pair's overhead units
     const int n = s_n[seq];
     const int p_start = 16 * a;
     const int p_end = min(16 * b, n);
@@ -798,7 +806,7 @@ void decode_flat_kernel(DecodeParams p) {
 
     const bool whole = a == 0 && b == tiles;
     const int item = seq * hkv + kh;
-    const int first_wg = wg_of_tile(item_base, total, nwg);
+    const int first_wg = wg_of_tile(tile_base, total, nwg);
     const int64_t slot = (int64_t)item + w;  // distinct for every (item, workgroup) pair
     for (int idx = tid; idx < G * D; idx += kThreads) {
       const int h = idx / D;
@@ -821,7 +829,7 @@ void decode_flat_kernel(DecodeParams p) {
       // scope) and every thread waits for its writes to complete before the
       // arrival is counted, so the last arriver, reading them back at agent
       // scope, sees all of them. No L2 write-back or invalidate is needed.
-      const int last_wg = wg_of_tile(item_base + tiles - 1, total, nwg);
+      const int last_wg = wg_of_tile(tile_base + tiles - 1, total, nwg);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (tid == 0)
@@ -867,7 +875,7 @@ void decode_flat_kernel(DecodeParams p) {
       }
     }
     __syncthreads();  // lds and s_last are reused by the next segment
-    pos = item_base + b;
+    pos = tile_base + b;
   }
   if (STEP) copy_new_rows<DT, D, G>(p, w + gridDim.x);
 }

@@ -39,6 +39,9 @@ struct DecodeParams {
   int max_context_len;
   int partition_size;
   int max_partitions;
+  // Balanced form: tiles of work charged for each (sequence, KV head) a
+  // workgroup's range touches, on top of its tiles (see decode_flat_kernel).
+  int seg_cost;
   int dtype;
   // Fused cache write (decode step form; null otherwise): token s of
   // new_key/new_value [S, Hkv, D] goes to slot_mapping[s] of the pools, and is
@@ -81,6 +84,11 @@ inline size_t flat_plan_lds_bytes(int num_seqs) { return size_t(3 * num_seqs + 1
 // from max_context_len), and at least one per compute unit. Defined in
 // pa_api.cpp.
 constexpr int kMinFlatTiles = 64;
+// Overhead units charged per (sequence, KV head) by the balanced plan. Swept on
+// MI355X over 0, 4, 8, 16, 32 tiles: 4 was best (GQA-4 bf16 decode 2% faster
+// than 0; 16 and more lengthen every workload).
+constexpr int kFlatSegmentCost = 4;
+int flat_segment_cost();
 int flat_grid_size(const void *kernel, int threads, size_t dynamic_lds, int64_t max_tiles);
 
 }  // namespace pa
