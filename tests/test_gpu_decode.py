@@ -228,6 +228,60 @@ def test_single_token_returns_its_value_exactly():
             assert torch.equal(out[s, h], v[blk, h // 2, 0])
 
 
+def _score_pattern(pattern, n, d, dtype):
+    """Per-position key magnitude t_i: with q rows of constant entries c and key rows
+    of constant entries t_i, the score of position i is c * t_i * sqrt(d).
+
+    Scores rise by about 3 (16-bit data) or 1.5 (f32 data) log2 units every 16
+    tokens. f32 ramps are centred on zero and its spikes are lower: an f32 score
+    near 130 in log2 units is itself resolved only to about 1.5e-5 (its spacing),
+    which no f32 kernel could keep within the 1e-5 output bound."""
+    i = np.arange(n, dtype=np.float64)
+    f32 = dtype == "f32"
+    step = (0.065 if f32 else 0.13) / math.sqrt(d)
+    mid = (n - 1) / 2 if f32 else 0.0
+    if pattern == "rising":
+        return step * (i - mid)
+    if pattern == "falling":
+        return step * (n - 1 - i - mid)
+    t = np.zeros(n)  # "spikes": flat, then a jump in the middle and a larger one near the end
+    t[n // 2] = (12.0 if f32 else 40.0) / math.sqrt(d)
+    t[max(n - 3, 0)] = (20.0 if f32 else 70.0) / math.sqrt(d)
+    return t
+
+
+@pytest.mark.parametrize("pattern", ["rising", "falling", "spikes"])
+@pytest.mark.parametrize("dtype,hq,hkv,d", [("f16", 8, 2, 128), ("bf16", 8, 2, 128),
+                                            ("f32", 4, 4, 64), ("f16", 4, 4, 64)])
+def test_scores_that_move_the_maximum(pattern, dtype, hq, hkv, d):
+    """Steadily rising scores make the kernel raise its reference maximum and
+    rescale its sums many times (every few 16-token rounds), in full and in masked
+    rounds; falling scores and isolated spikes cover the other orders. Each query
+    head of a group has its own slope (c = 1, 1.25, 1.5, 1.75)."""
+    lens = np.array([700, 333, 64, 17])
+    b = layouts.make_paged_batch(num_q_heads=hq, num_kv_heads=hkv, head_dim=d, dtype=dtype,
+                                 block_size=16, context_lens=lens, seed=21)
+    g = hq // hkv
+    c = 1.0 + 0.25 * (np.arange(hq) % g)
+    b.q = layouts.to_storage(np.broadcast_to(c[None, :, None], b.q.shape).astype(np.float32),
+                             dtype)
+    k = O.to_f64(b.k_cache, dtype).copy()
+    for s, n in enumerate(lens):
+        t = _score_pattern(pattern, int(n), d, dtype)
+        for pos in range(int(n)):
+            blk = b.block_tables[s, pos // 16]
+            k[blk, :, pos % 16, :] = t[pos]
+    b.k_cache = layouts.to_storage(k.astype(np.float32), dtype)
+    o64 = O.ref_decode(b.q, b.k_cache, b.v_cache, b.block_tables, b.context_lens, b.scale,
+                       dtype)
+    dev = layouts.to_device(b, "cuda")
+    for partition in (0, 64):
+        _, out = gpu_step(b, partition=partition, dev=dev, write=False)
+        rep = assert_decode_close(layouts.from_device(out, dtype), o64, dtype,
+                                  f"{pattern} {dtype} G{g} D{d} P={partition}")
+        _report(f"{pattern} {dtype} G{g} D{d} P={partition}", rep)
+
+
 def test_gqa_matches_repeated_mha():
     """GQA with G=4 and MHA on the repeated KV heads agree with the same oracle values."""
     b = layouts.scaled_config(3, max_seqs=3, max_len=500)
