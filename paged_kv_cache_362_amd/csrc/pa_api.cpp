@@ -177,6 +177,7 @@ int flat_grid_size(const void *kernel, int threads, size_t dynamic_lds, int64_t 
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, dynamic_lds) !=
           hipSuccess)
         return -1;
+      if (per_cu > kMaxFlatWgsPerCu) per_cu = kMaxFlatWgsPerCu;
       if (const char *e = std::getenv("PA_FLAT_WGS_PER_CU")) {  // tuning knob
         const int v = std::atoi(e);
         if (v > 0) per_cu = v;

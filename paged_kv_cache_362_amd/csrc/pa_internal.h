@@ -16,6 +16,12 @@ constexpr int kDefaultPartition = 256;
 // per-sequence tile counts lives in LDS) and this many workgroups.
 constexpr int kMaxPlanSeqs = 4096;
 constexpr int kMaxFlatWorkgroups = 2048;
+// Resident balanced-form workgroups per compute unit, at most. Measured on
+// MI355X: 3 beats the 4 that fit at 4 waves per SIMD (LLaMA-7B decode step
+// 101.6 -> 101.0 us, 13B 109.6 -> 107.7 us, three runs each): 12 waves per CU
+// keep ~190 KB of loads in flight, far above what the HBM latency needs, and
+// the longer ranges cut split pieces; 2 is slower.
+constexpr int kMaxFlatWgsPerCu = 3;
 
 struct DecodeParams {
   void *out;
