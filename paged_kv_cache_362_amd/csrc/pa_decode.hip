@@ -627,13 +627,14 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeParams p) {
 
 // ---------------------------------------------------------------------------
 // Balanced schedule: the (sequence, KV head, 16-token tile) space, flattened in
-// that order, is cut into gridDim.x equal ranges, one per workgroup. A
-// workgroup walks its range as segments (the part of one (sequence, KV head)
-// inside the range). A segment that is a whole (sequence, KV head) writes its
-// output rows; the pieces of a split one leave partials in the workspace and
-// the last workgroup to finish a piece combines them (log-sum-exp), so one
-// launch does the whole decode and every workgroup moves the same number of
-// tiles whatever the mix of context lengths.
+// that order with a fixed overhead charge in front of each (sequence, KV head),
+// is cut into gridDim.x equal ranges, one per workgroup. A workgroup walks its
+// range as segments (the part of one (sequence, KV head) inside the range). A
+// segment that is a whole (sequence, KV head) writes its output rows; the
+// pieces of a split one leave partials in the workspace and the last
+// workgroup to finish a piece combines them (log-sum-exp), so one launch does
+// the whole decode and every workgroup gets the same work (tiles plus segment
+// overheads) whatever the mix of context lengths.
 // ---------------------------------------------------------------------------
 
 // Partials shared between workgroups are written and read at agent scope:
