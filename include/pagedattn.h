@@ -55,8 +55,11 @@
  * PA_ERR_BAD_INDEX on a violation. A context length of 0 yields an all-zero
  * output row.
  *
- * Tuning: PA_FLAT_WGS_PER_CU (a positive integer) overrides the number of
- * workgroups per compute unit of the balanced form (default: as many as fit).
+ * Tuning (read once per process): PA_FLAT_WGS_PER_CU (a positive integer)
+ * overrides the number of workgroups per compute unit of the balanced form
+ * (default: as many as fit, at most 3). PA_FLAT_SEG_COST (0..1024) overrides
+ * the tiles of overhead the balanced form charges each (sequence, KV head) when
+ * it divides the work (default 4).
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
