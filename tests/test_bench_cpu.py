@@ -1,0 +1,63 @@
+"""Host-side contract of bench.py (CPU only; no kernel is launched)."""
+
+import json
+import os
+import re
+import subprocess
+import sys
+
+import bench
+from paged_kv_cache_362_amd import layouts
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+    assert res.stdout == ""
+
+
+def _record():
+    text = open(os.path.join(ROOT, bench.TRAFFIC_PROFILE)).read()
+    return json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
+
+
+def test_traffic_record_is_used_only_for_the_sources_it_was_taken_on(monkeypatch):
+    rec = _record()
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: rec["source_hash"])
+    assert bench.stored_traffic(rec["config"], rec["partition"], rec["fused"]) == \
+        rec["hbm_bytes_per_launch"]
+    # another workload, another form, or changed kernel sources: no traffic figure
+    assert bench.stored_traffic(rec["config"] + 1, rec["partition"], rec["fused"]) is None
+    assert bench.stored_traffic(rec["config"], 64, rec["fused"]) is None
+    assert bench.stored_traffic(rec["config"], rec["partition"], not rec["fused"]) is None
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    assert bench.stored_traffic(rec["config"], rec["partition"], rec["fused"]) is None
+
+
+def test_traffic_record_is_plausible():
+    """HBM bytes per launch within a few % of the workload's algorithmic bytes, and
+    consistent with the record's counters and calibration factors (stored to three
+    decimals, so to 0.1%)."""
+    from paged_kv_cache_362_amd import sizing
+    rec = _record()
+    b = layouts.make_config(rec["config"])
+    alg = (sizing.decode_algorithmic_bytes(b.context_lens, b.num_q_heads, b.num_kv_heads,
+                                           b.head_dim, b.elem_bytes, b.block_size) +
+           sizing.reshape_and_cache_bytes(b.slot_mapping.shape[0], b.num_kv_heads, b.head_dim,
+                                          b.elem_bytes))
+    assert 0.98 <= rec["hbm_bytes_per_launch"] / alg <= 1.10
+    got = (rec["fetch_kib_per_launch"] * rec["fetch_scale"] +
+           rec["write_kib_per_launch"] * rec["write_scale"]) * 1024
+    assert abs(got - rec["hbm_bytes_per_launch"]) <= 1e-3 * got
+
+
+def test_cpu_baseline_reports_what_it_timed():
+    b = layouts.make_config(1)
+    cb = bench.cpu_baseline(b, seconds=0.2)
+    assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["cores"] == 1
+    assert cb["value"] > 0 and cb["seconds"] >= 0.2
+    assert "oracle" in cb["sample"]
