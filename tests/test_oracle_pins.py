@@ -329,6 +329,44 @@ def pin_bf16_widening():
     assert list(O.bf16_round(x)) == [1.0, 1.0 + 2 ** -6, 1.0, -2.5]
 
 
+def _bf16_value_of_bits(bits):
+    """Value of bfloat16 bit patterns, through float32: a bfloat16 number is the
+    upper half of the float32 with the same sign, exponent and top mantissa bits."""
+    return (np.asarray(bits, np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def pin_bf16_spacing():
+    """ulp_bf16 is the gap to the next bfloat16 number, taken from bit patterns.
+
+    For a positive bfloat16 value x with bits b (and b + 1 in the same binade
+    or the first of the next), the spacing at x is value(b + 1) - value(b).
+    It decides how far a bfloat16 output of magnitude >= 1 may sit from the
+    rounded float64 result, so an exponent off by one would halve or double
+    that bound."""
+    xs = np.array([0.5, 0.75, 1.0, 1.5, 1.9921875, 2.0, 3.0, 3.890625, 7.5, 0.125])
+    bits = (xs.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint32)
+    assert np.array_equal(_bf16_value_of_bits(bits), xs)  # all are bfloat16 values
+    gap = _bf16_value_of_bits(bits + 1) - _bf16_value_of_bits(bits)
+    assert np.array_equal(O.ulp_bf16(xs), gap)
+    assert np.array_equal(O.ulp_bf16(-xs), gap)  # the spacing depends on |x| only
+    # closed forms: 8 significant bits, so 2**-7 on [1, 2) and 2**-6 on [2, 4)
+    assert list(O.ulp_bf16(np.array([1.0, 1.9921875, 2.0, -3.0, 0.5]))) == [
+        2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -6, 2.0 ** -8]
+
+
+def pin_bf16_round_matches_library():
+    """bf16_round agrees with torch's float32 -> bfloat16 conversion (round to
+    nearest, ties to even) on float32 inputs, ties included."""
+    rng = np.random.default_rng(11)
+    x32 = (rng.standard_normal(20000) * np.exp2(rng.integers(-6, 6, 20000))).astype(np.float32)
+    # exact ties: a bfloat16 value plus half its spacing
+    base = _bf16_value_of_bits(rng.integers(0x3C00, 0x4400, 2000).astype(np.uint32))
+    ties = (base + O.ulp_bf16(base) / 2).astype(np.float32)
+    x = np.concatenate([x32, ties, -ties]).astype(np.float64)
+    lib = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.bf16_round(x), lib)
+
+
 # --- multi-token (chunked-prefill) attention --------------------------------
 
 def _prefill_case(rng, hq, hkv, d, bs, lens, chunks):
@@ -468,6 +506,16 @@ def _right_aligned_gather(cache, table_row, context_len, kv_head, dtype):
     return O.to_f64(cache[blocks, kv_head, offs, :], dtype)
 
 
+def _ulp_exponent_off_by_one(x):
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    return np.exp2(np.floor(np.log2(ax)) - 6)
+
+
+def _bf16_round_seven_bits(x):
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.round(np.ldexp(m, 7)), e - 7)
+
+
 def _chunk_at_start(context_len, chunk_len, t):
     return t
 
@@ -481,6 +529,8 @@ def _causal_one_too_many(position):
 
 
 MUTANTS = {
+    "bf16_spacing_exponent_off_by_one": ("ulp_bf16", _ulp_exponent_off_by_one),
+    "bf16_round_seven_bits": ("bf16_round", _bf16_round_seven_bits),
     "prefill_chunk_at_start": ("query_position", _chunk_at_start),
     "prefill_excludes_own_key": ("visible_keys", _causal_off_by_one),
     "prefill_sees_next_key": ("visible_keys", _causal_one_too_many),
