@@ -1,16 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of one decode step of paged attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N]
 
 A step is the whole hot path over one batch: the cache write of the batch's
 new tokens and the attention over the paged cache. By default it is one launch
 (pa_decode_step: write and attention fused, balanced schedule); --separate
-times the two calls pa_reshape_and_cache + pa_decode instead. The default
-workload is the LLaMA-7B-layer MHA decode: 32 sequences, 32/32 heads of dim
-128, fp16, 16-token blocks, context lengths uniform in [128, 2048], scattered
-over a shuffled pool with 25% slack. Inputs are seeded synthetic data already
-resident in HBM.
+times the two calls pa_reshape_and_cache + pa_decode instead.
+
+Without --config, all five decode workloads are timed in one run, one after
+the other, and reported under "configs"; the headline value is workload 2, the
+LLaMA-7B-layer MHA decode: 32 sequences, 32/32 heads of dim 128, fp16, 16-token
+blocks, context lengths uniform in [128, 2048], scattered over a shuffled pool
+with 25% slack. The long-context workload is also timed without the flush.
+--config N times workload N alone (as a profiler run wants). Inputs are seeded
+synthetic data already resident in HBM.
 
 Timing: W untimed warm-up steps, then K timed steps. Before each step a 1 GiB
 buffer is read (outside the timed events) so the KV pools are not served from
@@ -37,8 +41,11 @@ sys.path.insert(0, ROOT)
 METRIC = "paged-decode KV-read GB/s & % of HBM peak; decode tokens/sec at batch"
 KERNEL_SOURCES = ["paged_kv_cache_362_amd/csrc/pa_decode.hip",
                   "paged_kv_cache_362_amd/csrc/pa_common.h",
-                  "paged_kv_cache_362_amd/csrc/pa_internal.h"]
+                  "paged_kv_cache_362_amd/csrc/pa_internal.h",
+                  "paged_kv_cache_362_amd/csrc/pa_api.cpp"]
 TRAFFIC_PROFILE = "profiles/decode_flat_kernel.llama7b_mha_decode.pmc.md"
+TRACE_PROFILE = "profiles/decode_flat_kernel.five_workloads.kernel_trace.md"
+HEADLINE_CONFIG = 2
 
 
 def parse_args(argv=None):
@@ -47,7 +54,9 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=None, choices=[1, 2, 3, 4, 5],
+                    help="time only this workload (default: all five, workload 2 the "
+                         "headline)")
     ap.add_argument("--partition", type=int, default=0,
                     help="0 = balanced single launch (default); >0 = fixed partitions")
     ap.add_argument("--separate", action="store_true",
@@ -57,6 +66,9 @@ def parse_args(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--calib-read", action="store_true",
+                    help="only measure plain read bandwidth (streamed and scattered tiles) "
+                         "with the calibration kernels; one JSON line")
     ap.add_argument("--paging-sweep", action="store_true",
                     help="decode on contiguous vs shuffled block tables at block sizes "
                          "8/16/32/64 (LLaMA-7B-layer shapes); prints one JSON line")
@@ -106,6 +118,80 @@ def calib_copy() -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
+
+
+def calib_read(args) -> dict:
+    """Read-bandwidth ceiling of this device, measured in the same process as the
+    decode would be: a 2 GiB buffer streamed once per launch, and the same
+    buffer read as whole tiles in shuffled and in sequential order (the tile
+    sizes of the decode workloads: 2, 4 and 8 KiB), with the decode kernel's
+    load shape (16-byte non-temporal loads, two register rounds in flight).
+    Each setting is timed with HIP events over `steps` launches after
+    `warmup`; the 2 GiB working set is 8x the last-level cache, so no flush is
+    needed."""
+    import ctypes
+    import numpy as np
+    import torch
+    from paged_kv_cache_362_amd import _lib
+
+    L = _lib.calib_lib()
+    dev = torch.device("cuda:0")
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    ptr = ctypes.c_void_p(buf.data_ptr())
+    sptr = ctypes.c_void_p(sink.data_ptr())
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+    def check(code):
+        if code != 0:
+            raise RuntimeError(f"calibration kernel returned {code}")
+
+    rows = []
+    for per_cu in (2, 3, 4, 8):
+        for nl in (4, 8, 16):
+            ms = timed(lambda: check(L.pa_calib_stream_read(ptr, nbytes, per_cu * cus, nl, sptr,
+                                                            stream)))
+            rows.append({"pattern": "stream", "wgs_per_cu": per_cu, "loads_in_flight": nl,
+                         "us": round(ms * 1e3, 1), "GBps": round(nbytes / ms / 1e6, 1)})
+    rng = np.random.default_rng(7)
+    for tile in (2048, 4096, 8192):
+        ntiles = nbytes // tile
+        orders = {"shuffled": rng.permutation(ntiles).astype(np.int32),
+                  "sequential": np.arange(ntiles, dtype=np.int32)}
+        for name, order in orders.items():
+            tiles = torch.from_numpy(order).to(dev)
+            tptr = ctypes.c_void_p(tiles.data_ptr())
+            for per_cu in (3, 4):
+                for nl in (8, 16):
+                    ms = timed(lambda: check(L.pa_calib_tile_read(
+                        ptr, ntiles, tptr, ntiles, tile, per_cu * cus, nl, sptr, stream)))
+                    rows.append({"pattern": f"tiles {tile // 1024} KiB {name}",
+                                 "wgs_per_cu": per_cu, "loads_in_flight": nl,
+                                 "us": round(ms * 1e3, 1),
+                                 "GBps": round((nbytes + 4 * ntiles) / ms / 1e6, 1)})
+            del tiles
+    best = {}
+    for r in rows:
+        if r["GBps"] > best.get(r["pattern"], {"GBps": 0})["GBps"]:
+            best[r["pattern"]] = r
+    return {"calib_read": rows,
+            "best_GBps": {k: v["GBps"] for k, v in best.items()},
+            "peak_GBps": 8000.0, "buffer_bytes": nbytes, "compute_units": cus,
+            "steps": args.steps, "warmup": args.warmup, "statistic": "median"}
 
 
 def paging_sweep(args) -> dict:
@@ -310,47 +396,38 @@ def cpu_baseline(batch, seconds: float) -> dict:
             "seconds": round(elapsed, 2), "host_cpus": len(os.sched_getaffinity(0))}
 
 
-def main(argv=None) -> int:
-    args = parse_args(argv)
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              f"(sequences or KV heads would shard across GPUs with no exchange inside "
-              f"attention, which is not built here)", file=sys.stderr)
-        return 2
+def kernel_trace_record():
+    """Per-workload kernel durations from the committed rocprofv3 trace, or
+    None unless they were taken on the current kernel sources."""
+    path = os.path.join(ROOT, TRACE_PROFILE)
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec
+
+
+def time_workload(cfg: int, args, partition: int, separate: bool, flush_between: bool,
+                  batch=None) -> dict:
+    """Time `args.steps` steps of one workload (after `args.warmup`), each
+    bracketed by HIP events on the launch stream. Returns the per-step times
+    and the workload's byte counts."""
     import numpy as np
     import torch
-
-    if args.calib_copy:
-        calib_copy()
-        return 0
-    if args.paging_sweep:
-        print(json.dumps(paging_sweep(args)), flush=True)
-        return 0
-    if args.block_ops:
-        print(json.dumps(block_ops(args)), flush=True)
-        return 0
-    if args.prefill:
-        print(json.dumps(prefill_bench(args)), flush=True)
-        return 0
-
     from paged_kv_cache_362_amd import layouts, ops, sizing
-    from paged_kv_cache_362_amd.layouts import CONFIGS
 
-    spec = CONFIGS[args.config]
-    t_gen = time.perf_counter()
-    b = layouts.make_config(args.config)
-    gen_s = time.perf_counter() - t_gen
+    b = batch if batch is not None else layouts.make_config(cfg)
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     t = layouts.to_device(b, dev)
-    s, hq, hkv, d = b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim
-    tdtype = t["q"].dtype
-    part = args.partition
     out = torch.empty_like(t["q"])
-    ws = ops.new_workspace(s, hq, hkv, d, b.max_context_len, tdtype, dev, part)
-    flush = None if args.no_flush else torch.ones(1 << 28, dtype=torch.float32, device=dev)
-
-    fused = not args.separate and part == 0
+    ws = ops.new_workspace(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                           b.max_context_len, t["q"].dtype, dev, partition)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev) if flush_between else None
+    fused = not separate and partition == 0
 
     def step(ev=None):
         if ev is not None:
@@ -365,7 +442,7 @@ def main(argv=None) -> int:
             if ev is not None:
                 ev[1].record()
             ops.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
-                       t["context_lens"], b.scale, b.max_context_len, out, ws, part)
+                       t["context_lens"], b.scale, b.max_context_len, out, ws, partition)
         if ev is not None:
             ev[2].record()
 
@@ -374,9 +451,7 @@ def main(argv=None) -> int:
             flush.amax()
         step()
     torch.cuda.synchronize()
-
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.steps):
         if flush is not None:
@@ -384,24 +459,132 @@ def main(argv=None) -> int:
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-
     step_ms = np.array([e[0].elapsed_time(e[2]) for e in events])
-    # fused: the one launch; separate: the cache write, then the decode
     first_ms = step_ms if fused else np.array([e[0].elapsed_time(e[1]) for e in events])
     dec_ms = step_ms if fused else np.array([e[1].elapsed_time(e[2]) for e in events])
-
     e = b.elem_bytes
-    lens = b.context_lens
-    decode_bytes = sizing.decode_algorithmic_bytes(lens, hq, hkv, d, e, b.block_size)
-    cache_bytes = sizing.reshape_and_cache_bytes(b.slot_mapping.shape[0], hkv, d, e)
-    step_bytes = decode_bytes + cache_bytes
-    kv_bytes = sizing.kv_read_bytes(lens, hkv, d, e)
-    ms = float(step_ms.mean())
-    value = step_bytes / (ms * 1e-3) / 1e9
-    kernel_bytes = step_bytes if fused else decode_bytes
-    achieved = kernel_bytes / (float(dec_ms.mean()) * 1e-3) / 1e9
+    decode_bytes = sizing.decode_algorithmic_bytes(b.context_lens, b.num_q_heads,
+                                                   b.num_kv_heads, b.head_dim, e, b.block_size)
+    unique_decode_bytes = sizing.decode_algorithmic_bytes(
+        b.context_lens, b.num_q_heads, b.num_kv_heads, b.head_dim, e, b.block_size,
+        unique_tokens=sizing.unique_context_tokens(b.block_tables, b.context_lens,
+                                                   b.block_size))
+    cache_bytes = sizing.reshape_and_cache_bytes(b.slot_mapping.shape[0], b.num_kv_heads,
+                                                 b.head_dim, e)
+    del t, out, ws, flush
+    torch.cuda.empty_cache()
+    return {"batch": b, "fused": fused, "step_ms": step_ms, "first_ms": first_ms,
+            "dec_ms": dec_ms, "wall": wall, "decode_bytes": decode_bytes,
+            "unique_decode_bytes": unique_decode_bytes, "cache_bytes": cache_bytes}
 
-    traffic = stored_traffic(args.config, part, fused)
+
+def workload_summary(cfg: int, r: dict, trace) -> dict:
+    """Per-workload fields of the JSON line: event times, bytes, rates and the
+    kernel-trace fraction from the committed profile (when current)."""
+    import numpy as np
+    from paged_kv_cache_362_amd import sizing
+
+    b = r["batch"]
+    step_bytes = r["decode_bytes"] + r["cache_bytes"]
+    unique_step_bytes = r["unique_decode_bytes"] + r["cache_bytes"]
+    ms = float(r["step_ms"].mean())
+    gbps = step_bytes / ms / 1e6
+    row = {
+        "workload": b.name, "dtype": b.dtype, "num_seqs": b.num_seqs,
+        "heads": f"{b.num_q_heads}/{b.num_kv_heads}", "head_dim": b.head_dim,
+        "block_size": b.block_size, "context_tokens": int(b.context_lens.sum()),
+        "step_us_mean": round(ms * 1e3, 2),
+        "step_us_median": round(float(np.median(r["step_ms"])) * 1e3, 2),
+        "step_us_min": round(float(r["step_ms"].min()) * 1e3, 2),
+        "algorithmic_bytes": int(step_bytes),
+        "GBps": round(gbps, 1),
+        "pct_hbm_peak": round(100 * gbps / sizing.HBM_PEAK_GBPS, 2),
+        "tokens_per_s": round(b.num_seqs / (ms * 1e-3), 1),
+    }
+    if r["unique_decode_bytes"] != r["decode_bytes"]:
+        ugbps = unique_step_bytes / ms / 1e6
+        row.update({"unique_bytes": int(unique_step_bytes), "GBps_unique": round(ugbps, 1),
+                    "pct_hbm_peak_unique": round(100 * ugbps / sizing.HBM_PEAK_GBPS, 2)})
+    roof_bytes = unique_step_bytes
+    row["roofline_bytes"] = "unique" if roof_bytes != step_bytes else "algorithmic"
+    row["frac_events"] = round(roof_bytes / ms / 1e6 / sizing.HBM_PEAK_GBPS, 4)
+    kus = (trace or {}).get("kernel_avg_us", {}).get(str(cfg))
+    row["kernel_trace_us"] = kus
+    row["frac_kernel"] = (round(roof_bytes / (kus * 1e-6) / 1e9 / sizing.HBM_PEAK_GBPS, 4)
+                          if kus else None)
+    return row
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(sequences or KV heads would shard across GPUs with no exchange inside "
+              f"attention, which is not built here)", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    if args.calib_copy:
+        calib_copy()
+        return 0
+    if args.calib_read:
+        print(json.dumps(calib_read(args)), flush=True)
+        return 0
+    if args.paging_sweep:
+        print(json.dumps(paging_sweep(args)), flush=True)
+        return 0
+    if args.block_ops:
+        print(json.dumps(block_ops(args)), flush=True)
+        return 0
+    if args.prefill:
+        print(json.dumps(prefill_bench(args)), flush=True)
+        return 0
+
+    from paged_kv_cache_362_amd import layouts, sizing
+
+    torch.cuda.set_device(0)
+    part = args.partition
+    # One workload (--config N), or the headline workload first and then the
+    # other four, each timed in the same process.
+    headline = args.config if args.config is not None else HEADLINE_CONFIG
+    others = [] if args.config is not None else [c for c in (1, 2, 3, 4, 5) if c != headline]
+    t_gen = time.perf_counter()
+    hb = layouts.make_config(headline)
+    gen_s = time.perf_counter() - t_gen
+    trace = kernel_trace_record() if part == 0 and not args.separate else None
+    res = {headline: time_workload(headline, args, part, args.separate, not args.no_flush, hb)}
+    for c in others:
+        res[c] = time_workload(c, args, part, args.separate, not args.no_flush)
+    if others and not args.no_flush and 4 in res:
+        # the long-context pools (67 MB) fit in the 256 MB last-level cache: the
+        # same steps without the flush show what the flush removes
+        res["4_no_flush"] = time_workload(4, args, part, args.separate, False)
+
+    r = res[headline]
+    b = r["batch"]
+    fused = r["fused"]
+    s, hq, hkv, d = b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim
+    step_bytes = r["decode_bytes"] + r["cache_bytes"]
+    ms = float(r["step_ms"].mean())
+    value = step_bytes / (ms * 1e-3) / 1e9
+    kernel_bytes = step_bytes if fused else r["decode_bytes"]
+    achieved = kernel_bytes / (float(r["dec_ms"].mean()) * 1e-3) / 1e9
+    kv_bytes = sizing.kv_read_bytes(b.context_lens, hkv, d, b.elem_bytes)
+    hrow = workload_summary(headline, r, trace)
+    traffic = stored_traffic(headline, part, fused)
+    kus = hrow["kernel_trace_us"] if fused else None
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2),
+                "peak": sizing.HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / sizing.HBM_PEAK_GBPS, 4),
+                "frac_basis": "HIP events around the launch (kernel plus its dispatch)",
+                "frac_kernel": (round(kernel_bytes / (kus * 1e-6) / 1e9 / sizing.HBM_PEAK_GBPS, 4)
+                                if kus else None),
+                "frac_kernel_basis": ("committed rocprofv3 kernel trace of the current sources "
+                                      f"({TRACE_PROFILE}), average duration {kus} us"
+                                      if kus else "no kernel trace of the current sources"),
+                "kernel": "decode_flat_kernel" if part == 0 else "decode_partition_kernel",
+                "traffic": traffic}
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -416,35 +599,41 @@ def main(argv=None) -> int:
         "dtype": b.dtype,
         "data": "synthetic",
         "config": {
-            "workload": spec.name, "config": args.config, "num_seqs": s, "num_q_heads": hq,
+            "workload": b.name, "config": headline, "num_seqs": s, "num_q_heads": hq,
             "num_kv_heads": hkv, "head_dim": d, "block_size": b.block_size,
-            "context_tokens": int(lens.sum()), "max_context_len": b.max_context_len,
+            "context_tokens": int(b.context_lens.sum()), "max_context_len": b.max_context_len,
             "num_blocks": b.num_blocks,
             "decode_form": ("balanced" if part == 0 else f"fixed partitions of {part}") +
                            (", cache write fused (pa_decode_step)" if fused
                             else ", cache write separate (pa_reshape_and_cache)"),
             "parallelism": "none (1 GPU)",
-            "cache_flush_between_steps": flush is not None,
+            "cache_flush_between_steps": not args.no_flush,
         },
         "pct_hbm_peak": round(100 * value / sizing.HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(s / (ms * 1e-3), 1),
         "kv_read_GBps": round(kv_bytes / (ms * 1e-3) / 1e9, 2),
         "kernel_ms": {("decode_step" if fused else "reshape_and_cache"):
-                      round(float(first_ms.mean()), 5),
-                      "decode": round(float(dec_ms.mean()), 5),
-                      "decode_median": round(float(np.median(dec_ms)), 5),
-                      "step_median": round(float(np.median(step_ms)), 5),
-                      "step_min": round(float(step_ms.min()), 5)},
-        "bytes_per_step": {"algorithmic": int(step_bytes), "decode": int(decode_bytes),
+                      round(float(r["first_ms"].mean()), 5),
+                      "decode": round(float(r["dec_ms"].mean()), 5),
+                      "decode_median": round(float(np.median(r["dec_ms"])), 5),
+                      "step_median": round(float(np.median(r["step_ms"])), 5),
+                      "step_min": round(float(r["step_ms"].min()), 5)},
+        "bytes_per_step": {"algorithmic": int(step_bytes), "decode": int(r["decode_bytes"]),
                            "kv": int(kv_bytes)},
-        "wall_s_timed_loop": round(wall, 4),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2),
-                     "peak": sizing.HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / sizing.HBM_PEAK_GBPS, 4),
-                     "kernel": "decode_flat_kernel" if part == 0 else "decode_partition_kernel",
-                     "traffic": traffic},
+        "wall_s_timed_loop": round(r["wall"], 4),
+        "roofline": roofline,
         "input_gen_s": round(gen_s, 2),
     }
+    if others:
+        cfgs = {str(c): workload_summary(c, res[c], trace) for c in (1, 2, 3, 4, 5)}
+        if "4_no_flush" in res:
+            nf = workload_summary(4, res["4_no_flush"], None)
+            cfgs["4"]["no_flush"] = {k: nf[k] for k in ("step_us_mean", "step_us_median",
+                                                       "GBps", "pct_hbm_peak")}
+        line["configs"] = cfgs
+        line["configs_note"] = ("every workload timed in this run, same protocol as the "
+                                "headline; % of the 8 TB/s peak uses unique bytes where "
+                                "sequences share blocks (the copy-on-write prefix)")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
     print(json.dumps(line), flush=True)

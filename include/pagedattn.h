@@ -49,7 +49,7 @@
  * non-zero status nothing was enqueued (except PA_ERR_HIP, which reports a
  * launch failure). Values that live in device memory (table entries in
  * [0, num_blocks), 1 <= context_lens[s] <= max_context_len, distinct slots,
- * zero arrival counters) are preconditions; they are checked only when the
+ * zero workspace counters) are preconditions; they are checked only when the
  * environment variable PA_DEBUG is set to a non-zero value, in which case the
  * call copies them to the host (synchronising the stream) and returns
  * PA_ERR_BAD_INDEX on a violation. A context length of 0 yields an all-zero
@@ -138,8 +138,8 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  *         equal share of all (sequence, KV head, 16-token tile) work, however
  *         unequal the context lengths; a (sequence, KV head) split between
  *         workgroups is combined by the last of them to finish. Used for
- *         num_seqs <= 4096; beyond that the call falls back to fixed
- *         partitions of 256 tokens.
+ *         num_seqs <= 4096 (and while that work stays below 2^31 tiles);
+ *         beyond that the call falls back to fixed partitions of 256 tokens.
  *   P > 0 fixed partitions of P tokens (a multiple of 16, at most 4096): one
  *         workgroup per (partition, KV head, sequence), then a second launch
  *         combines the partitions.

@@ -3,7 +3,10 @@
     python -m paged_kv_cache_362_amd.build [--jobs N] [--verbose]
 
 Every source under csrc/ is compiled to an object in _build/ (in parallel),
-then linked into paged_kv_cache_362_amd/libpagedattn.so. Always rebuilds.
+then linked into paged_kv_cache_362_amd/libpagedattn.so. The read-bandwidth
+calibration kernels (calib/, include/pa_calib.h) the benchmark runs beside the
+decode are linked into their own paged_kv_cache_362_amd/libpacalib.so. Always
+rebuilds both.
 """
 
 from __future__ import annotations
@@ -18,9 +21,11 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
+CALIB = os.path.join(PKG, "calib")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
+CALIB_LIB = os.path.join(PKG, "libpacalib.so")
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -49,8 +54,8 @@ def hipcc() -> str:
     return path
 
 
-def sources() -> list[str]:
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+def sources(folder: str = CSRC) -> list[str]:
+    return sorted(os.path.join(folder, f) for f in os.listdir(folder)
                   if f.endswith((".hip", ".cpp")))
 
 
@@ -70,20 +75,26 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 2)))
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int | None = None, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    calib = sources(CALIB)
+    jobs = jobs or min(len(srcs) + len(calib), max(1, (os.cpu_count() or 2)))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + calib))
+    _link(objs[:len(srcs)], LIB, verbose)
+    _link(objs[len(srcs):], CALIB_LIB, verbose)
     return LIB
 
 

@@ -75,11 +75,20 @@ int32_t num_partitions(int32_t max_context_len, int32_t partition) {
   return np < 1 ? 1 : np;
 }
 
+// Upper bound of the balanced form's work units (tiles plus the overhead
+// charged per (sequence, KV head)); the kernel keeps unit positions in int32.
+bool flat_units_fit(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
+  const int64_t per_item = (int64_t(max_context_len) + 15) / 16 + pa::flat_segment_cost();
+  return int64_t(num_seqs) * num_kv_heads * per_item < (int64_t(1) << 31) - 1;
+}
+
 // The form a call takes: the balanced single launch, or fixed partitions of
 // `*partition` tokens (the default size when the balanced form cannot plan
-// this many sequences).
-bool use_balanced(int32_t num_seqs, int32_t requested, int32_t *partition) {
-  if (requested == 0 && num_seqs <= pa::kMaxPlanSeqs) {
+// this many sequences, or this much work).
+bool use_balanced(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                  int32_t requested, int32_t *partition) {
+  if (requested == 0 && num_seqs <= pa::kMaxPlanSeqs &&
+      flat_units_fit(num_seqs, num_kv_heads, max_context_len)) {
     *partition = 0;
     return true;
   }
@@ -103,8 +112,9 @@ WsLayout workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_
   WsLayout w;
   int32_t partition = 0;
   w.counters = round_up(size_t(num_seqs) * size_t(num_kv_heads) * sizeof(int32_t));
-  if (use_balanced(num_seqs, requested, &partition)) {
+  if (use_balanced(num_seqs, num_kv_heads, max_context_len, requested, &partition)) {
     const size_t group = size_t(num_q_heads / num_kv_heads);
+    // one slot per (item, workgroup) piece: at most items + workgroups of them
     w.slots = size_t(num_seqs) * num_kv_heads + pa::kMaxFlatWorkgroups;
     w.width = group * head_dim;
     w.stats = w.slots * group;
@@ -455,7 +465,8 @@ int32_t decode_impl(void *out, const void *q, const void *k_cache, const void *v
     return PA_ERR_BAD_SHAPE;
   if (!partition_ok(partition_size)) return PA_ERR_BAD_SHAPE;
   int32_t part = 0;
-  const bool balanced = use_balanced(num_seqs, partition_size, &part);
+  const bool balanced = use_balanced(num_seqs, num_kv_heads, max_context_len, partition_size,
+                                     &part);
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return PA_ERR_NULL_POINTER;

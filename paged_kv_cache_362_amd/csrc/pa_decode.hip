@@ -628,13 +628,14 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // Balanced schedule: the (sequence, KV head, 16-token tile) space, flattened in
 // that order with a fixed overhead charge in front of each (sequence, KV head),
-// is cut into gridDim.x equal ranges, one per workgroup. A workgroup walks its
-// range as segments (the part of one (sequence, KV head) inside the range). A
-// segment that is a whole (sequence, KV head) writes its output rows; the
+// is cut into equal ranges of `sz` units, one per workgroup. A workgroup walks
+// its range as segments (the part of one (sequence, KV head) inside the range).
+// A segment that is a whole (sequence, KV head) writes its output rows; the
 // pieces of a split one leave partials in the workspace and the last
 // workgroup to finish a piece combines them (log-sum-exp), so one launch does
 // the whole decode and every workgroup gets the same work (tiles plus segment
-// overheads) whatever the mix of context lengths.
+// overheads) whatever the mix of context lengths. Unit positions fit in int32:
+// the host takes this form only when an upper bound of the units does.
 // ---------------------------------------------------------------------------
 
 // Partials shared between workgroups are written and read at agent scope:
@@ -647,10 +648,29 @@ __device__ __forceinline__ float fetch(const float *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Workgroup holding flattened tile x (ranges [floor(w T / N), floor((w+1) T / N)),
-// all non-empty since N <= T).
-__device__ __forceinline__ int wg_of_tile(int64_t x, int64_t total, int nwg) {
-  return (int)(((x + 1) * nwg - 1) / total);
+__device__ __forceinline__ int uniform_i32(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Coordinates of the segment of a range [.., end) that starts at unit pos,
+// inside sequence seq: KV head kh, its tiles [a, b) (b <= a: the range ends in
+// the item's overhead units), the item's tile count and first tile unit. All
+// wave-uniform; read from the plan in LDS, so the caller can re-derive them
+// after the streaming loop instead of keeping them in registers across it.
+struct SegCoords {
+  int kh, a, b, tiles, tile_base;
+};
+
+__device__ __forceinline__ SegCoords seg_coords(const int *s_tc, int seq, int hkv, int cost,
+                                                int pos, int end) {
+  SegCoords c;
+  const int tc0 = uniform_i32(s_tc[seq]);
+  const int units = uniform_i32(s_tc[seq + 1]) - tc0;
+  c.tiles = units - cost;
+  const int seq_base = hkv * tc0;
+  c.kh = (pos - seq_base) / units;
+  c.tile_base = seq_base + c.kh * units + cost;  // the item's overhead units, then its tiles
+  c.a = max(pos - c.tile_base, 0);
+  c.b = min(end - c.tile_base, c.tiles);
+  return c;
 }
 
 // Decode step: this step's K/V rows go into the pools one (sequence, KV head)
@@ -658,7 +678,8 @@ __device__ __forceinline__ int wg_of_tile(int64_t x, int64_t total, int nwg) {
 // launch reads them back from the pools: the attention takes them from LDS
 // (see consume_round). A workgroup loads its first pair at the start, next to
 // the plan's loads, and stores it once the plan is done; further pairs (more
-// pairs than workgroups) are copied after its attention work.
+// pairs than workgroups) are copied after its attention work. The slot is
+// range-checked at the store, so both loads are in flight together.
 template <int DT, int D, int G> struct NewRowCopy {
   static constexpr int kChunks = DecodeShape<DT, D, G, 1>::ROWB / 16;
   u32x4 data;
@@ -668,14 +689,13 @@ template <int DT, int D, int G> struct NewRowCopy {
     const int tid = threadIdx.x;
     if (pair < p.num_seqs * p.num_kv_heads && tid < 2 * kChunks) {
       slot = p.slot_mapping[pair / p.num_kv_heads];
-      if (slot >= p.num_slots) slot = -1;  // out of range: nothing is written
       const int64_t src = ((int64_t)pair * kChunks + tid % kChunks) * 16;
       data = load_chunk(tid < kChunks ? p.new_key : p.new_value, src);
     }
   }
   __device__ __forceinline__ void store(const DecodeParams &p, int pair) const {
     const int tid = threadIdx.x;
-    if (slot < 0) return;
+    if (slot < 0 || slot >= p.num_slots) return;  // negative: skip; too large: never write outside
     const int kh = pair % p.num_kv_heads;
     const int bshift = p.block_shift;
     const int64_t row = (((int64_t)(slot >> bshift) * p.num_kv_heads + kh) << bshift) +
@@ -692,6 +712,73 @@ __device__ __forceinline__ void copy_new_rows(const DecodeParams &p, int first) 
     NewRowCopy<DT, D, G> row;
     row.load(p, pair);
     row.store(p, pair);
+  }
+}
+
+// The last piece of a split (sequence, KV head) to arrive combines the
+// partials of pieces first..last (slots item + j) in one pass with a running
+// maximum, a batch of pieces at a time. Every output element a thread owns
+// (G * D / 256 of them, or one) is handled in the same batch, so all of its
+// requests are in flight together: the partials are read at agent scope, and
+// each round trip from there costs microseconds while the memory system is
+// busy.
+template <int DT, int G, int D>
+__device__ __forceinline__ void combine_pieces(const DecodeParams &p, typename Store<DT>::T *out,
+                                               int item, int first, int last) {
+  constexpr int E = (G * D + kThreads - 1) / kThreads;  // elements per thread
+  constexpr int PB = E >= 4 ? 2 : E == 2 ? 4 : 8;        // pieces per batch: 24 requests a thread
+  int tid = threadIdx.x;
+  // Opaque to the optimiser, so these addresses are formed here rather than
+  // hoisted out of the segment loop and kept (or spilled) across it.
+  asm volatile("" : "+v"(tid));
+  float mrun[E], num[E], den[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    mrun[e] = -INFINITY;
+    num[e] = 0.0f;
+    den[e] = 0.0f;
+  }
+  for (int j0 = first; j0 <= last; j0 += PB) {
+    float mj[E][PB], lj[E][PB], aj[E][PB];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int idx = min(tid + e * kThreads, G * D - 1);
+      const int h = idx / D, d = idx % D;
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {  // `last` is uniform: no request past the last piece
+        const int64_t sl = (int64_t)item + j0 + u;
+        const bool have = j0 + u <= last;
+        mj[e][u] = have ? fetch(p.ws_m + sl * G + h) : -INFINITY;
+        lj[e][u] = have ? fetch(p.ws_l + sl * G + h) : 0.0f;
+        aj[e][u] = have ? fetch(p.ws_acc + (sl * G + h) * D + d) : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float mnew = mrun[e];
+#pragma unroll
+      for (int u = 0; u < PB; ++u)
+        if (j0 + u <= last) mnew = fmaxf(mnew, mj[e][u]);
+      const float sc = mrun[e] == -INFINITY ? 0.0f : fast_exp2(mrun[e] - mnew);
+      num[e] *= sc;
+      den[e] *= sc;
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        if (j0 + u > last) continue;
+        const float f = fast_exp2(mj[e][u] - mnew);
+        num[e] = fmaf(f, aj[e][u], num[e]);
+        den[e] = fmaf(f, lj[e][u], den[e]);
+      }
+      mrun[e] = mnew;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int idx = tid + e * kThreads;
+    if (idx < G * D) {
+      const int h = idx / D, d = idx % D;
+      out[((int64_t)item * G + h) * D + d] = Store<DT>::cvt(num[e] / den[e]);
+    }
   }
 }
 
@@ -758,7 +845,7 @@ void decode_flat_kernel(DecodeParams p) {
     carry += total;
     __syncthreads();
   }
-  const int64_t total = (int64_t)hkv * carry;
+  const int total = hkv * carry;  // < 2^31 (checked on the host)
 
   if (STEP) first_row.store(p, w);
 
@@ -768,46 +855,42 @@ void decode_flat_kernel(DecodeParams p) {
       for (int i = tid; i < num_q_heads * D; i += kThreads)
         out[(int64_t)s * num_q_heads * D + i] = Store<DT>::cvt(0.0f);
 
-  // With fewer tiles than workgroups only the first `total` take part, so every
-  // range below is non-empty (the combine counts on that).
-  const int nwg = (int)min((int64_t)gridDim.x, total);
+  // Ranges of sz = ceil(total / grid) units; the last takes what is left and
+  // workgroups past it take none, so every range that exists is non-empty
+  // (the piece count of the combine counts on that). Range of unit x: x / sz.
+  const int nwg = min((int)gridDim.x, total);
   if (w >= nwg) {
     if (STEP) copy_new_rows<DT, D, G>(p, w + gridDim.x);
     return;
   }
-  const int64_t start = (int64_t)w * total / nwg;
-  const int64_t end = (int64_t)(w + 1) * total / nwg;
+  const int start = (int)((int64_t)w * total / nwg);
+  const int end = (int)((int64_t)(w + 1) * total / nwg);
 
-  // The sequence holding flattened tile `start`.
+  // The sequence holding unit `start`.
   for (int s = tid; s < S; s += kThreads)
-    if ((int64_t)hkv * s_tc[s] <= start && start < (int64_t)hkv * s_tc[s + 1]) s_found = s;
+    if (hkv * s_tc[s] <= start && start < hkv * s_tc[s + 1]) s_found = s;
   __syncthreads();
-  int seq = __builtin_amdgcn_readfirstlane(s_found);
+  int seq = uniform_i32(s_found);
 
-  int64_t pos = start;
+  int pos = start;
   while (pos < end) {
-    while (pos >= (int64_t)hkv * s_tc[seq + 1]) ++seq;  // skips empty sequences
-    const int units = s_tc[seq + 1] - s_tc[seq];
-    const int tiles = units - cost;
-    const int64_t seq_base = (int64_t)hkv * s_tc[seq];
-    const int kh = (int)((pos - seq_base) / units);
-    const int64_t item_base = seq_base + (int64_t)kh * units;  // its overhead units, then its tiles
-    const int64_t tile_base = item_base + cost;
-    const int a = (int)max(pos - tile_base, (int64_t)0);
-    const int b = (int)min(end - tile_base, (int64_t)tiles);
-    if (b <= a) break;  // the range ends inside this pair's overhead units
-    const int n = s_n[seq];
-    const int p_start = 16 * a;
-    const int p_end = min(16 * b, n);
-
-    int new_pos = -1;  // decode step: the written position, when this segment ends the item
-    if (STEP && b == tiles && s_slot[seq] >= 0) new_pos = n - 1;
-    run_segment<DT, D, G, NT, BS8>(p, seq, kh, p_start, p_end, wave, lds, new_pos);
+    while (pos >= hkv * s_tc[seq + 1]) ++seq;  // skips empty sequences
+    {
+      const SegCoords c = seg_coords(s_tc, seq, hkv, cost, pos, end);
+      if (c.b <= c.a) break;  // the range ends inside this pair's overhead units
+      const int n = s_n[seq];
+      int new_pos = -1;  // decode step: the written position, when this segment ends the item
+      if (STEP && c.b == c.tiles && s_slot[seq] >= 0) new_pos = n - 1;
+      run_segment<DT, D, G, NT, BS8>(p, seq, c.kh, 16 * c.a, min(16 * c.b, n), wave, lds,
+                                     new_pos);
+    }
     __syncthreads();
+    const SegCoords c = seg_coords(s_tc, seq, hkv, cost, pos, end);
+    const int kh = c.kh, a = c.a, b = c.b, tiles = c.tiles, tile_base = c.tile_base;
 
     const bool whole = a == 0 && b == tiles;
     const int item = seq * hkv + kh;
-    const int first_wg = wg_of_tile(tile_base, total, nwg);
+    const int first_w = (int)(((int64_t)(tile_base + 1) * nwg - 1) / total);
     const int64_t slot = (int64_t)item + w;  // distinct for every (item, workgroup) pair
     for (int idx = tid; idx < G * D; idx += kThreads) {
       const int h = idx / D;
@@ -830,47 +913,15 @@ void decode_flat_kernel(DecodeParams p) {
       // scope) and every thread waits for its writes to complete before the
       // arrival is counted, so the last arriver, reading them back at agent
       // scope, sees all of them. No L2 write-back or invalidate is needed.
-      const int last_wg = wg_of_tile(tile_base + tiles - 1, total, nwg);
+      const int last_w = (int)(((int64_t)(tile_base + tiles) * nwg - 1) / total);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (tid == 0)
         s_last = __hip_atomic_fetch_add(p.ws_count + item, 1, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT) == last_wg - first_wg;
+                                        __HIP_MEMORY_SCOPE_AGENT) == last_w - first_w;
       __syncthreads();
+      if (s_last) combine_pieces<DT, G, D>(p, out, item, first_w, last_w);
       if (s_last) {
-        for (int idx = tid; idx < G * D; idx += kThreads) {
-          const int h = idx / D;
-          const int d = idx % D;
-          // One pass over the contributors with a running maximum, eight at a
-          // time so that their loads are in flight together.
-          float mrun = -INFINITY, num = 0.0f, den = 0.0f;
-          for (int j0 = first_wg; j0 <= last_wg; j0 += 8) {
-            float mj[8], lj[8], aj[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              const int64_t sl = (int64_t)item + min(j0 + u, last_wg);
-              mj[u] = fetch(p.ws_m + sl * G + h);
-              lj[u] = fetch(p.ws_l + sl * G + h);
-              aj[u] = fetch(p.ws_acc + (sl * G + h) * D + d);
-            }
-            float mnew = mrun;
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-              if (j0 + u <= last_wg) mnew = fmaxf(mnew, mj[u]);
-            const float sc = mrun == -INFINITY ? 0.0f : fast_exp2(mrun - mnew);
-            num *= sc;
-            den *= sc;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-              if (j0 + u > last_wg) continue;
-              const float f = fast_exp2(mj[u] - mnew);
-              num = fmaf(f, aj[u], num);
-              den = fmaf(f, lj[u], den);
-            }
-            mrun = mnew;
-          }
-          out[((int64_t)item * G + h) * D + d] = Store<DT>::cvt(num / den);
-        }
         if (tid == 0)  // leave the counter zero for the next call
           __hip_atomic_store(p.ws_count + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }

@@ -53,22 +53,41 @@ def blocks_that_fit(free_bytes: int, bytes_per_block: int) -> int:
 
 def decode_algorithmic_bytes(context_lens: Sequence[int], num_q_heads: int,
                              num_kv_heads: int, head_dim: int, elem_bytes: int,
-                             block_size: int, unique_blocks: int | None = None) -> int:
+                             block_size: int, unique_blocks: int | None = None,
+                             unique_tokens: int | None = None) -> int:
     """Bytes one decode call must move.
 
     Each attended token's K and V row for every KV head, the queries read and
     the outputs written once, one 4-byte table entry per block attended and
-    one 4-byte length per sequence. With ``unique_blocks`` the KV term counts
-    each distinct physical block once (prefix shared by several sequences).
+    one 4-byte length per sequence. With ``unique_tokens`` the KV term counts
+    each distinct cache slot once (a prefix shared by several sequences, whose
+    tables name the same blocks, is read from HBM once); ``unique_blocks``
+    counts whole distinct blocks instead (exact when every block is full).
     """
     num_seqs = len(context_lens)
-    if unique_blocks is None:
+    if unique_tokens is not None:
+        kv = unique_tokens * num_kv_heads * head_dim * 2 * elem_bytes
+    elif unique_blocks is None:
         kv = sum(int(n) for n in context_lens) * num_kv_heads * head_dim * 2 * elem_bytes
     else:
         kv = unique_blocks * block_size * num_kv_heads * head_dim * 2 * elem_bytes
     q_and_out = 2 * num_seqs * num_q_heads * head_dim * elem_bytes
     tables = 4 * sum(blocks_needed(int(n), block_size) for n in context_lens)
     return kv + q_and_out + tables + 4 * num_seqs
+
+
+def unique_context_tokens(block_tables, context_lens: Sequence[int], block_size: int) -> int:
+    """Distinct cache slots the sequences attend to: position i of sequence s
+    lives in slot block_tables[s][i // B] * B + i % B, and sequences that share
+    blocks ([INFRA] §4.3, copy-on-write prefix sharing) share those slots."""
+    slots = set()
+    for s, n in enumerate(context_lens):
+        row = block_tables[s]
+        for j in range(blocks_needed(int(n), block_size)):
+            used = min(block_size, int(n) - j * block_size)
+            base = int(row[j]) * block_size
+            slots.update(range(base, base + used))
+    return len(slots)
 
 
 def kv_read_bytes(context_lens: Sequence[int], num_kv_heads: int, head_dim: int,

@@ -60,6 +60,7 @@ def _floats(n):
 
 def test_workspace_size(lib):
     # balanced form: counters, then (S * Hkv + 2048) slots of G * (D + 2) floats
+    # (one per piece: at most one per (sequence, KV head) plus one per workgroup)
     assert lib.pa_decode_workspace_size(32, 32, 32, 128, 2048, 0, F16) == \
         _counters(32, 32) + _floats((32 * 32 + 2048) * 130)
     assert lib.pa_decode_workspace_size(64, 32, 8, 128, 4096, 0, BF16) == \
@@ -107,7 +108,7 @@ def test_decode_rejects_bad_arguments_before_launch(lib):
     assert _decode(lib, maxlen=50, part=16, ws=16, wsb=10) == WS
     assert _decode(lib, maxlen=50) == NULLP  # the balanced form always needs one
     assert _decode(lib, maxlen=50, ws=16, wsb=1000) == WS
-    assert _decode(lib, maxlen=50, ws=24, wsb=1 << 20) == UNSUP  # misaligned workspace
+    assert _decode(lib, maxlen=50, ws=24, wsb=1 << 24) == UNSUP  # misaligned workspace
     assert _decode(lib, S=0, q=None, out=None) == OK  # empty batch: no work, no launch
 
 
@@ -195,3 +196,35 @@ def test_prefill_rejects_bad_arguments_before_launch(lib):
     assert call(scale=float("nan")) == UNSUP
     assert call(T=0, out=None, q=None) == OK  # nothing to do
     assert call(Lmax=0, out=None) == OK
+
+
+
+CALIB_HEADER = os.path.join(ROOT, "include", "pa_calib.h")
+
+
+def test_calibration_library_exports_its_header_and_checks_arguments():
+    """libpacalib.so (the read-bandwidth kernels the benchmark runs beside the
+    decode) exports what include/pa_calib.h declares and rejects bad arguments
+    on the host, before any launch."""
+    if not os.path.exists(_lib.CALIB_LIB_PATH):
+        pytest.fail("libpacalib.so is not built (python -m paged_kv_cache_362_amd.build)")
+    text = re.sub(r"/\*.*?\*/", "", open(CALIB_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(pa_calib_[a-z0-9_]+)\s*\(", text)))
+    assert names == sorted(_lib.CALIB_SIGNATURES)
+    cl = _lib.calib_lib()
+    for n in names:
+        assert hasattr(cl, n)
+    s = cl.pa_calib_stream_read
+    assert s(None, 16384, 0, 8, 16, None) == 1
+    assert s(16, 16384, 0, 8, None, None) == 1
+    assert s(16, 1000, 0, 8, 16, None) == 2       # not a multiple of 16 KiB
+    assert s(24, 16384, 0, 8, 16, None) == 2      # misaligned
+    assert s(16, 16384, 0, 0, 16, None) == 2      # loads in flight out of range
+    assert s(16, 16384, 0, 17, 16, None) == 2
+    t = cl.pa_calib_tile_read
+    assert t(16, 4, None, 4, 4096, 0, 8, 16, None) == 1
+    assert t(16, 4, 16, 4, 3000, 0, 8, 16, None) == 2   # not a power of two
+    assert t(16, 4, 16, 4, 512, 0, 8, 16, None) == 2    # below 1 KiB
+    assert t(16, 4, 16, 4, 1 << 17, 0, 8, 16, None) == 2  # above 64 KiB
+    assert t(16, 0, 16, 4, 4096, 0, 8, 16, None) == 2   # empty buffer
+    assert t(16, 4, 16, 0, 4096, 0, 8, 16, None) == 0   # nothing to read: no launch

@@ -61,3 +61,17 @@ def test_cpu_baseline_reports_what_it_timed():
     assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["cores"] == 1
     assert cb["value"] > 0 and cb["seconds"] >= 0.2
     assert "oracle" in cb["sample"]
+
+
+def test_kernel_trace_record_is_used_only_for_the_sources_it_was_taken_on(monkeypatch, tmp_path):
+    """frac_kernel comes from the committed kernel trace only while the kernel
+    sources hash to the record's source_hash."""
+    rec = {"source_hash": "abcd" * 4, "kernel_avg_us": {"2": 97.0}}
+    prof = tmp_path / "trace.md"
+    prof.write_text("# trace\n\n```json\n" + json.dumps(rec) + "\n```\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "TRACE_PROFILE", "trace.md")
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: rec["source_hash"])
+    assert bench.kernel_trace_record()["kernel_avg_us"]["2"] == 97.0
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    assert bench.kernel_trace_record() is None
