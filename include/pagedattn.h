@@ -80,7 +80,9 @@ enum {
   PA_ERR_WORKSPACE_TOO_SMALL = 4,
   PA_ERR_HIP = 5,                /* the HIP runtime reported an error */
   PA_ERR_BAD_INDEX = 6,          /* PA_DEBUG: a device-side precondition failed */
-  PA_ERR_BAD_POINTER = 7         /* memory the GPU cannot address (e.g. pageable host) */
+  PA_ERR_BAD_POINTER = 7,        /* memory the GPU cannot address (e.g. pageable host) */
+  PA_ERR_SCRATCH_TOO_SMALL = 8   /* pa_decode_step_noalloc: the call needs more scratch
+                                    than PA_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Element types of q, out, key, value and the pools (all the same). */
@@ -197,6 +199,45 @@ int32_t pa_decode_step(void *out, const void *q, const void *key,
                        int32_t max_blocks_per_seq, int32_t max_context_len,
                        int32_t dtype, void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/* Bytes of the static device scratch of pa_decode_step_noalloc (per GPU). */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * pa_decode_step_noalloc - pa_decode_step for callers that cannot allocate
+ * device memory: code under HIP graph capture, serving loops that must not
+ * call hipMalloc, harnesses that forbid it. No workspace argument: the decode's
+ * scratch (counters and split partials) is a static device array of
+ * PA_NOALLOC_SCRATCH_BYTES (32 MiB) inside the library, one per GPU, held
+ * until the process ends. The call allocates and frees nothing.
+ *
+ * Arguments, layouts, preconditions and the result are those of
+ * pa_decode_step; out, the pools and key/value come out bit-identical to a
+ * pa_decode_step call with a zero-filled workspace. The call enqueues a small
+ * kernel that clears the counters, then the decode step, on `stream`.
+ * Returns PA_ERR_SCRATCH_TOO_SMALL (nothing enqueued) when
+ * pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+ * max_context_len, 0, dtype) exceeds PA_NOALLOC_SCRATCH_BYTES (e.g. 64
+ * sequences of 8 KV heads, GQA-4, head_dim 128 need 5.3 MB), otherwise the
+ * codes of pa_decode_step. The first call on a GPU looks up that GPU's copy
+ * of the array (hipGetSymbolAddress); later calls reuse the address.
+ *
+ * Every call on one GPU shares its array: calls that overlap in time on that
+ * GPU (on different streams, or from several host threads) race on it and
+ * give wrong results; order them on one stream. PA_DEBUG checks copy to the
+ * host and synchronise, so they must stay off under graph capture.
+ */
+int32_t pa_decode_step_noalloc(void *out, const void *q, const void *key,
+                               const void *value, void *k_cache, void *v_cache,
+                               const int32_t *slot_mapping,
+                               const int32_t *block_tables,
+                               const int32_t *context_lens, float scale,
+                               int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks,
+                               int32_t max_blocks_per_seq,
+                               int32_t max_context_len, int32_t dtype,
+                               void *stream);
 
 /*
  * pa_copy_blocks - copy whole physical blocks inside the pools

@@ -28,6 +28,9 @@ SIGNATURES = {
     "pa_decode_step": (_i32, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _f32, _i32,
                               _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _ptr, _size,
                               _ptr]),
+    "pa_decode_step_noalloc": (_i32, [_ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr, _f32,
+                                      _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                      _ptr]),
     "pa_copy_blocks": (_i32, [_ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _i32, _i32, _ptr]),
     "pa_swap_blocks": (_i32, [_ptr, _ptr, _ptr, _ptr, _ptr, _i32, _i32, _i32, _i32, _i32,
                               _i32, _i32, _ptr]),

@@ -21,7 +21,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
 constexpr size_t kAlign = 256;
 
 bool debug_checks() {
@@ -231,6 +231,7 @@ const char *pa_status_str(int32_t status) {
     case PA_ERR_HIP: return "HIP runtime error";
     case PA_ERR_BAD_INDEX: return "device-side index precondition violated (PA_DEBUG)";
     case PA_ERR_BAD_POINTER: return "memory is neither GPU memory nor pinned host memory";
+    case PA_ERR_SCRATCH_TOO_SMALL: return "the call needs more scratch than the static array holds";
   }
   return "unknown status";
 }
@@ -445,6 +446,9 @@ struct StepArgs {
   void *k_cache = nullptr;
   void *v_cache = nullptr;
   const int32_t *slot_mapping = nullptr;
+  // The scratch is the library's static array (pa_decode_step_noalloc), not
+  // the workspace arguments; its counters are cleared on the stream first.
+  bool static_scratch = false;
 };
 
 int32_t decode_impl(void *out, const void *q, const void *k_cache, const void *v_cache,
@@ -480,6 +484,12 @@ int32_t decode_impl(void *out, const void *q, const void *k_cache, const void *v
                                         max_context_len, partition_size);
   const int32_t max_parts = balanced ? 1 : num_partitions(max_context_len, part);
   const bool needs_ws = balanced || max_parts > 1;
+  if (step.static_scratch) {
+    if (lay.total > pa::kNoallocScratchBytes) return PA_ERR_SCRATCH_TOO_SMALL;
+    workspace = pa::noalloc_scratch();
+    if (workspace == nullptr) return PA_ERR_HIP;
+    workspace_bytes = pa::kNoallocScratchBytes;
+  }
   if (needs_ws) {
     if (!workspace) return PA_ERR_NULL_POINTER;
     if (workspace_bytes < lay.total) return PA_ERR_WORKSPACE_TOO_SMALL;
@@ -520,13 +530,20 @@ int32_t decode_impl(void *out, const void *q, const void *k_cache, const void *v
         if (v != want) return PA_ERR_BAD_INDEX;
       }
     }
-    if (balanced) {  // the arrival counters must be zero
+    if (balanced && !step.static_scratch) {  // the arrival counters must be zero
       std::vector<int32_t> cnt(size_t(num_seqs) * num_kv_heads);
       st = sync_copy_to_host(cnt.data(), workspace, sizeof(int32_t) * cnt.size(), s);
       if (st != PA_OK) return st;
       for (int32_t c : cnt)
         if (c != 0) return PA_ERR_BAD_INDEX;
     }
+  }
+
+  if (step.static_scratch && balanced) {
+    // The static scratch keeps the last call's contents: zero the arrival
+    // counters (lay.counters bytes, within the scratch by the check above).
+    if (pa::launch_clear_words(workspace, int(lay.counters / sizeof(int32_t)), s) != hipSuccess)
+      return PA_ERR_HIP;
   }
 
   if (fused && !balanced) {
@@ -610,6 +627,26 @@ int32_t pa_decode_step(void *out, const void *q, const void *key, const void *va
                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_blocks_per_seq, max_context_len, 0, dtype, workspace, workspace_bytes,
                      stream, step);
+}
+
+int32_t pa_decode_step_noalloc(void *out, const void *q, const void *key, const void *value,
+                               void *k_cache, void *v_cache, const int32_t *slot_mapping,
+                               const int32_t *block_tables, const int32_t *context_lens,
+                               float scale, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t max_context_len, int32_t dtype, void *stream) {
+  if (num_seqs > 0 && !slot_mapping) return PA_ERR_NULL_POINTER;
+  StepArgs step;
+  step.key = key;
+  step.value = value;
+  step.k_cache = k_cache;
+  step.v_cache = v_cache;
+  step.slot_mapping = slot_mapping;
+  step.static_scratch = true;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_blocks_per_seq, max_context_len, 0, dtype, nullptr, 0, stream, step);
 }
 
 }  // extern "C"

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pagedattn.h"
+
 namespace pa {
 
 // Largest partition (tokens) a decode workgroup of the fixed-partition form
@@ -95,6 +97,13 @@ constexpr int kMinFlatTiles = 64;
 // than 0; 16 and more lengthen every workload).
 constexpr int kFlatSegmentCost = 4;
 int flat_segment_cost();
+
+// Static scratch of pa_decode_step_noalloc (pa_noalloc.hip): its bytes, this
+// device's address of it (looked up once per device; nullptr on failure), and
+// a kernel that zeroes its first n int32 words on `stream`.
+constexpr size_t kNoallocScratchBytes = size_t(PA_NOALLOC_SCRATCH_BYTES);
+void *noalloc_scratch();
+hipError_t launch_clear_words(void *words, int n, hipStream_t stream);
 int flat_grid_size(const void *kernel, int threads, size_t dynamic_lds, int64_t max_tiles);
 
 }  // namespace pa

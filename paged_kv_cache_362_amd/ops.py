@@ -18,7 +18,7 @@ DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 PA_OK = 0
 STATUS = {0: "PA_OK", 1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_BAD_SHAPE", 3: "PA_ERR_UNSUPPORTED",
           4: "PA_ERR_WORKSPACE_TOO_SMALL", 5: "PA_ERR_HIP", 6: "PA_ERR_BAD_INDEX",
-          7: "PA_ERR_BAD_POINTER"}
+          7: "PA_ERR_BAD_POINTER", 8: "PA_ERR_SCRATCH_TOO_SMALL"}
 
 
 class PagedAttentionError(RuntimeError):
@@ -180,6 +180,37 @@ def decode_step(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
         int(max_context_len), dtype_code(q.dtype), _dev_ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(q))
     _check("pa_decode_step", code)
+    return out
+
+
+def decode_step_noalloc(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                        k_cache: torch.Tensor, v_cache: torch.Tensor,
+                        slot_mapping: torch.Tensor, block_tables: torch.Tensor,
+                        context_lens: torch.Tensor, scale: float, max_context_len: int,
+                        out: torch.Tensor) -> torch.Tensor:
+    """decode_step with the library's static scratch (``pa_decode_step_noalloc``):
+    nothing is allocated, so ``out`` must be given. Calls that overlap on one
+    GPU share that scratch and must be ordered on one stream."""
+    _on_gpu(q, k_cache, v_cache, block_tables, context_lens, out, key, value, slot_mapping)
+    _require(q.dim() == 3 and out.shape == q.shape and out.dtype == q.dtype,
+             "q [S, Hq, D] and out of the same shape and dtype")
+    _require(k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "pools must be [N, Hkv, B, D]")
+    _require(q.dtype == k_cache.dtype == v_cache.dtype == key.dtype == value.dtype,
+             "one dtype for q, key, value and the pools")
+    _require(key.shape == value.shape == (q.shape[0], k_cache.shape[1], q.shape[2]),
+             "key/value must be [S, Hkv, D]")
+    for t, name in ((slot_mapping, "slot_mapping"), (context_lens, "context_lens")):
+        _require(t.dtype == torch.int32 and t.shape == (q.shape[0],), f"{name} must be int32 [S]")
+    _require(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+             block_tables.shape[0] == q.shape[0], "block_tables must be int32 [S, M]")
+    s, hq, d = q.shape
+    n, hkv, bs, _ = k_cache.shape
+    code = lib().pa_decode_step_noalloc(
+        _dev_ptr(out), _dev_ptr(q), _dev_ptr(key), _dev_ptr(value), _dev_ptr(k_cache),
+        _dev_ptr(v_cache), _dev_ptr(slot_mapping), _dev_ptr(block_tables),
+        _dev_ptr(context_lens), float(scale), s, hq, hkv, d, bs, n, block_tables.shape[1],
+        int(max_context_len), dtype_code(q.dtype), _stream(q))
+    _check("pa_decode_step_noalloc", code)
     return out
 
 

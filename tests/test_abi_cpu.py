@@ -44,8 +44,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings_and_version(lib):
-    assert lib.pa_abi_version() == 3
-    for code in range(8):
+    assert lib.pa_abi_version() == 4
+    for code in range(9):
         assert lib.pa_status_str(code)
     assert lib.pa_status_str(99) == b"unknown status"
 
@@ -228,3 +228,33 @@ def test_calibration_library_exports_its_header_and_checks_arguments():
     assert t(16, 4, 16, 4, 1 << 17, 0, 8, 16, None) == 2  # above 64 KiB
     assert t(16, 0, 16, 4, 4096, 0, 8, 16, None) == 2   # empty buffer
     assert t(16, 4, 16, 0, 4096, 0, 8, 16, None) == 0   # nothing to read: no launch
+
+
+def test_noalloc_step_rejects_bad_arguments_before_launch(lib):
+    """pa_decode_step_noalloc: the checks of pa_decode_step, plus a call whose
+    scratch would not fit the static array (PA_NOALLOC_SCRATCH_BYTES, 32 MiB),
+    all answered on the host before any device call."""
+    f = lib.pa_decode_step_noalloc
+    SCRATCH_TOO_SMALL = 8
+
+    def call(**kw):
+        a = dict(out=16, q=16, key=16, value=16, k=16, v=16, slots=16, bt=16, cl=16,
+                 scale=0.125, S=1, Hq=4, Hkv=4, D=64, B=16, N=4, M=4, maxlen=50, dtype=F16,
+                 stream=None)
+        a.update(kw)
+        return f(a["out"], a["q"], a["key"], a["value"], a["k"], a["v"], a["slots"], a["bt"],
+                 a["cl"], a["scale"], a["S"], a["Hq"], a["Hkv"], a["D"], a["B"], a["N"],
+                 a["M"], a["maxlen"], a["dtype"], a["stream"])
+
+    assert call(slots=None) == NULLP
+    assert call(key=None) == NULLP
+    assert call(value=24) == UNSUP  # misaligned
+    assert call(Hq=6) == SHAPE
+    assert call(maxlen=65) == SHAPE
+    assert call(S=0, q=None, out=None, slots=None) == OK
+    # 4096 sequences x 8 KV heads, GQA-8, head_dim 256, bf16: ~318 MB of partials
+    big = dict(S=4096, Hq=64, Hkv=8, D=256, B=16, N=1 << 20, M=256, maxlen=4096, dtype=BF16)
+    need = lib.pa_decode_workspace_size(4096, 64, 8, 256, 4096, 0, BF16)
+    assert need > 32 << 20
+    assert call(**big) == SCRATCH_TOO_SMALL
+    assert lib.pa_status_str(SCRATCH_TOO_SMALL) != b"unknown status"
