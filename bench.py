@@ -427,7 +427,10 @@ def time_workload(cfg: int, args, partition: int, separate: bool, flush_between:
     ws = ops.new_workspace(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
                            b.max_context_len, t["q"].dtype, dev, partition)
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev) if flush_between else None
-    fused = not separate and partition == 0
+    # The fused step needs each new token to be its sequence's last attended
+    # position; the tiny workload writes into a fresh block instead, so it is
+    # timed as the two calls.
+    fused = not separate and partition == 0 and layouts.new_tokens_are_last(b)
 
     def step(ev=None):
         if ev is not None:
@@ -500,6 +503,8 @@ def workload_summary(cfg: int, r: dict, trace) -> dict:
         "GBps": round(gbps, 1),
         "pct_hbm_peak": round(100 * gbps / sizing.HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(b.num_seqs / (ms * 1e-3), 1),
+        "step_form": ("one launch (pa_decode_step)" if r["fused"]
+                      else "two launches (pa_reshape_and_cache + pa_decode)"),
     }
     if r["unique_decode_bytes"] != r["decode_bytes"]:
         ugbps = unique_step_bytes / ms / 1e6

@@ -309,6 +309,10 @@ int32_t pa_swap_blocks(const void *src_k, const void *src_v, void *dst_k, void *
  * No workspace; nothing allocated. Device-resident preconditions (monotone
  * query_start_loc ending at num_tokens, chunk and context lengths, table
  * entries in range) are checked only under PA_DEBUG=1 (PA_ERR_BAD_INDEX).
+ * Without it, table entries are clamped into [0, num_blocks) (no read leaves
+ * the pools), and a sequence whose chunk lies outside [0, num_tokens), is
+ * longer than its context, or whose context is longer than its table row gets
+ * no output rows. max_blocks_per_seq * block_size must stay below 2^31.
  * Tokens of sequences with L_s = 0 do not exist; nothing else is written.
  */
 int32_t pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,

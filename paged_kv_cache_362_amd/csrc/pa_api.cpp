@@ -375,6 +375,7 @@ int32_t pa_prefill(void *out, const void *q, const void *k_cache, const void *v_
     return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PA_OK;
   if (max_query_len > num_tokens) return PA_ERR_BAD_SHAPE;
+  if (int64_t(max_blocks_per_seq) * block_size > (int64_t(1) << 31) - 1) return PA_ERR_BAD_SHAPE;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc)
     return PA_ERR_NULL_POINTER;
   if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -413,11 +414,13 @@ int32_t pa_prefill(void *out, const void *q, const void *k_cache, const void *v_
   p.query_start_loc = query_start_loc;
   p.scale_log2 = float(double(scale) * 1.4426950408889634074);
   p.num_seqs = num_seqs;
+  p.num_tokens = num_tokens;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
   p.block_size = block_size;
   p.block_shift = __builtin_ctz(unsigned(block_size));
   p.max_blocks_per_seq = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
   p.q_tiles = int(q_tiles);
   return pa::launch_prefill(p, dtype, head_dim, max_query_len, s) == hipSuccess ? PA_OK
                                                                                : PA_ERR_HIP;

@@ -23,11 +23,13 @@ struct PrefillParams {
   const int32_t *query_start_loc;  // [S + 1]
   float scale_log2;                // scale * log2(e)
   int num_seqs;
+  int num_tokens;                  // rows of q and out
   int num_q_heads;
   int num_kv_heads;
   int block_size;
   int block_shift;                 // log2(block_size)
   int max_blocks_per_seq;
+  int num_blocks;                  // pool size: table entries are clamped into [0, num_blocks)
   int q_tiles;                     // query-row tiles per (sequence, KV head)
 };
 

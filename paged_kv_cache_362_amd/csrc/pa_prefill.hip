@@ -161,6 +161,7 @@ template <int D> struct Stager {
   const char *vbase;
   const int32_t *table;  // this sequence's table row
   uint32_t blk_bytes;    // Hkv * B * D * 2: one physical block of all KV heads
+  uint32_t max_block;    // num_blocks - 1: table entries are clamped to it
   uint32_t bshift, bmask;
   uint32_t last_pos;     // context length - 1
   uint32_t key[S::KCH_T], col[S::KCH_T];  // item's key in the tile and byte column
@@ -187,7 +188,11 @@ template <int D> struct Stager {
 
   __device__ void load_table(KVStage<D> &r, int j) const {
 #pragma unroll
-    for (int u = 0; u < S::KCH_T; ++u) r.phys[u] = uint32_t(table[pos_of(j, key[u]) >> bshift]);
+    for (int u = 0; u < S::KCH_T; ++u) {
+      // never address outside the pool, whatever the table holds
+      const int e = table[pos_of(j, key[u]) >> bshift];
+      r.phys[u] = min(uint32_t(max(e, 0)), max_block);
+    }
   }
   __device__ void load_kv(KVStage<D> &r, int j) const {
 #pragma unroll
@@ -243,6 +248,13 @@ void prefill_kernel(PrefillParams p) {
   const int rows = L * G;
   if (qt * S::ROWS >= rows) return;
   const int n = p.context_lens[seq];
+  // A chunk outside the packed tokens, a chunk longer than its context, or a
+  // context longer than its table row breaks the call's preconditions
+  // (checked on the host only under PA_DEBUG): such a sequence gets no output
+  // rather than accesses outside q, out or its table row. Positions below are
+  // then in [0, n), so the uint32 ones are safe.
+  if (q0 < 0 || q0 > p.num_tokens - L || L > n || n > (p.max_blocks_per_seq << p.block_shift))
+    return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -276,6 +288,7 @@ void prefill_kernel(PrefillParams p) {
   st.vbase = reinterpret_cast<const char *>(p.v_cache) + int64_t(kh) * p.block_size * D * 2;
   st.table = p.block_tables + int64_t(seq) * p.max_blocks_per_seq;
   st.blk_bytes = uint32_t(p.num_kv_heads) * p.block_size * D * 2;
+  st.max_block = uint32_t(p.num_blocks - 1);
   st.bshift = p.block_shift;
   st.bmask = p.block_size - 1;
   st.last_pos = n - 1;

@@ -336,6 +336,22 @@ def make_prefill_workload(name: str, seed: int = 7) -> PrefillBatch:
     return make_prefill_batch(seed=seed, name=name, **PREFILL_WORKLOADS[name])
 
 
+def new_tokens_are_last(b: PagedBatch) -> bool:
+    """Whether each sequence's new token is written to the slot of its last
+    attended position (context_lens[s] - 1), which the fused decode step
+    (pa_decode_step) requires. The tiny workload writes its token into a fresh
+    block outside the attended context instead."""
+    for s, n in enumerate(b.context_lens):
+        n = int(n)
+        slot = int(b.slot_mapping[s])
+        if n < 1 or slot < 0:
+            continue
+        last = n - 1
+        if slot != int(b.block_tables[s, last // b.block_size]) * b.block_size + last % b.block_size:
+            return False
+    return True
+
+
 def make_config(config: int, seed: int | None = None, poison: bool = False) -> PagedBatch:
     """One of the five named workloads at full size."""
     spec = CONFIGS[config]

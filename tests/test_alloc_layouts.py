@@ -213,3 +213,12 @@ def test_swap_needs_room_and_equal_blocks():
     assert a.pool is dev and a.blocks == [0, 1, 2] and small.num_free == 2
     with pytest.raises(ValueError):
         a.move_to(BlockPool(8, range(8), block_size_hint=32))
+
+
+def test_new_tokens_are_last_positions_except_in_the_tiny_workload():
+    """The fused decode step needs every new token at its sequence's last
+    attended position; workloads 2-5 write there, the tiny one writes into a
+    fresh block outside its 50-token context."""
+    assert not layouts.new_tokens_are_last(layouts.make_config(1))
+    for c in (2, 4):
+        assert layouts.new_tokens_are_last(layouts.make_config(c))

@@ -148,3 +148,28 @@ def test_prefill_random_shapes(seed):
     got = _run(b)
     assert_decode_close(got, _oracle(b), dtype,
                         f"seed {seed}: {dtype} D{d} Hkv{hkv} G{g} B{bs} lens {lens} chunks {chunks}")
+
+
+def test_prefill_bad_device_values_stay_inside_their_sequence():
+    """Without PA_DEBUG the host cannot see device-resident values. Table
+    entries outside the pool are clamped into it, and a sequence whose chunk
+    is longer than its context gets no output rows; neither disturbs the
+    other sequences, whose rows still match the oracle."""
+    b = layouts.make_prefill_batch(num_q_heads=8, num_kv_heads=4, head_dim=64, dtype="f16",
+                                   block_size=16, context_lens=[200, 150, 90],
+                                   chunk_lens=[40, 30, 20], seed=91, poison=False)
+    want = _oracle(b)
+    t = layouts.prefill_to_device(b)
+    t["block_tables"][1, 0] = b.paged.num_blocks + 5   # past the pool
+    t["block_tables"][1, 3] = -3                        # negative
+    t["context_lens"][2] = 10                           # shorter than its 20-token chunk
+    out = torch.full_like(t["q"], 7.0)
+    ops.prefill(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                t["query_start_loc"], b.scale, b.max_query_len, out)
+    torch.cuda.synchronize()
+    got = layouts.from_device(out, b.dtype)
+    qsl = b.query_start_loc
+    rows0 = slice(qsl[0], qsl[1])
+    assert_decode_close(got[rows0], want[rows0], "f16", "untouched sequence")
+    assert np.all(got[qsl[2]:qsl[3]] == np.float16(7.0)), "refused chunk was written"
+    assert np.isfinite(got[qsl[1]:qsl[2]].astype(np.float32)).all()
