@@ -43,7 +43,7 @@ KERNEL_SOURCES = ["paged_kv_cache_362_amd/csrc/pa_decode.hip",
                   "paged_kv_cache_362_amd/csrc/pa_common.h",
                   "paged_kv_cache_362_amd/csrc/pa_internal.h",
                   "paged_kv_cache_362_amd/csrc/pa_api.cpp"]
-TRAFFIC_PROFILE = "profiles/decode_flat_kernel.llama7b_mha_decode.pmc.md"
+TRAFFIC_PROFILE = "profiles/decode_flat_kernel.five_workloads.pmc.md"
 TRACE_PROFILE = "profiles/decode_flat_kernel.five_workloads.kernel_trace.md"
 HEADLINE_CONFIG = 2
 
@@ -69,6 +69,10 @@ def parse_args(argv=None):
     ap.add_argument("--calib-read", action="store_true",
                     help="only measure plain read bandwidth (streamed and scattered tiles) "
                          "with the calibration kernels; one JSON line")
+    ap.add_argument("--startup-sweep", action="store_true",
+                    help="decode of one workload (--config, default 4) with its device "
+                         "context lengths capped from 0 up: fixed cost per launch and "
+                         "marginal read rate; one JSON line")
     ap.add_argument("--paging-sweep", action="store_true",
                     help="decode on contiguous vs shuffled block tables at block sizes "
                          "8/16/32/64 (LLaMA-7B-layer shapes); prints one JSON line")
@@ -93,8 +97,8 @@ def stored_traffic(config: int, partition: int, fused: bool):
     """HBM bytes per launch of the timed decode kernel, from the committed
     counter profile.
 
-    Returns None unless the profile was taken on this workload and form with
-    the current kernel sources.
+    Returns None unless the profile holds this workload, was taken on this
+    form and on the current kernel sources.
     """
     path = os.path.join(ROOT, TRAFFIC_PROFILE)
     if not os.path.exists(path):
@@ -103,10 +107,10 @@ def stored_traffic(config: int, partition: int, fused: bool):
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if (rec.get("source_hash") != kernel_source_hash() or rec.get("config") != config
-            or rec.get("partition") != partition or rec.get("fused", False) != fused):
+    if (rec.get("source_hash") != kernel_source_hash() or rec.get("partition") != partition
+            or rec.get("fused", False) != fused):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("records", {}).get(str(config), {}).get("hbm_bytes_per_launch")
 
 
 def calib_copy() -> None:
@@ -192,6 +196,63 @@ def calib_read(args) -> dict:
             "best_GBps": {k: v["GBps"] for k, v in best.items()},
             "peak_GBps": 8000.0, "buffer_bytes": nbytes, "compute_units": cus,
             "steps": args.steps, "warmup": args.warmup, "statistic": "median"}
+
+
+def startup_sweep(args) -> dict:
+    """Fixed and per-byte cost of one decode launch: the same workload and
+    launch (grid sized from max_context_len, balanced pa_decode) with every
+    device context length cut to a cap, from 0 (start-up only: launch, plan,
+    exit) to the full lengths. A straight line through the longer caps gives
+    the marginal read rate; its intercept is what each call costs whatever it
+    reads (start-up chain, pipeline fill, split-head combine, tail)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_362_amd import layouts, ops, sizing
+
+    cfg = args.config or 4
+    dev = torch.device("cuda:0")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    b = layouts.make_config(cfg)
+    t = layouts.to_device(b, dev)
+    out = torch.empty_like(t["q"])
+    ws = ops.new_workspace(b.num_seqs, b.num_q_heads, b.num_kv_heads, b.head_dim,
+                           b.max_context_len, t["q"].dtype, dev)
+    rows = []
+    caps = [c for c in (0, 16, 64, 256, 1024, 2048, 4096, 8192) if c < b.max_context_len]
+    for cap in caps + [None]:
+        lens = b.context_lens if cap is None else np.minimum(b.context_lens, cap).astype(np.int32)
+        cl = torch.from_numpy(np.ascontiguousarray(lens)).to(dev)
+
+        def call():
+            ops.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"], cl, b.scale,
+                       b.max_context_len, out, ws)
+        for _ in range(args.warmup):
+            flush.amax()
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for e0, e1 in ev:
+            flush.amax()
+            e0.record()
+            call()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+        nbytes = sizing.decode_algorithmic_bytes(lens, b.num_q_heads, b.num_kv_heads,
+                                                 b.head_dim, b.elem_bytes, b.block_size)
+        rows.append({"len_cap": cap if cap is not None else "none", "bytes": int(nbytes),
+                     "us_mean": round(float(ms.mean()) * 1e3, 2),
+                     "us_median": round(float(np.median(ms)) * 1e3, 2)})
+    big = [r for r in rows if r["bytes"] >= rows[-1]["bytes"] / 8]
+    x = np.array([r["bytes"] for r in big], float)
+    y = np.array([r["us_mean"] for r in big], float)
+    slope, icpt = np.polyfit(x, y, 1) if len(big) >= 2 else (float("nan"), float("nan"))
+    return {"startup_sweep": rows, "workload": b.name, "config": cfg,
+            "fit_over_caps_with_at_least_1/8_of_the_bytes": {
+                "fixed_us": round(float(icpt), 2),
+                "marginal_GBps": round(1e-3 / float(slope), 1) if slope > 0 else None},
+            "steps": args.steps, "warmup": args.warmup, "statistic": "mean of HIP events",
+            "note": "lengths capped on the device only; grid, table and pools unchanged"}
 
 
 def paging_sweep(args) -> dict:
@@ -513,6 +574,8 @@ def workload_summary(cfg: int, r: dict, trace) -> dict:
     roof_bytes = unique_step_bytes
     row["roofline_bytes"] = "unique" if roof_bytes != step_bytes else "algorithmic"
     row["frac_events"] = round(roof_bytes / ms / 1e6 / sizing.HBM_PEAK_GBPS, 4)
+    traffic = stored_traffic(cfg, 0, r["fused"]) if trace is not None else None
+    row["hbm_traffic_bytes"] = traffic
     kus = (trace or {}).get("kernel_avg_us", {}).get(str(cfg))
     row["kernel_trace_us"] = kus
     row["frac_kernel"] = (round(roof_bytes / (kus * 1e-6) / 1e9 / sizing.HBM_PEAK_GBPS, 4)
@@ -535,6 +598,9 @@ def main(argv=None) -> int:
         return 0
     if args.calib_read:
         print(json.dumps(calib_read(args)), flush=True)
+        return 0
+    if args.startup_sweep:
+        print(json.dumps(startup_sweep(args)), flush=True)
         return 0
     if args.paging_sweep:
         print(json.dumps(paging_sweep(args)), flush=True)
