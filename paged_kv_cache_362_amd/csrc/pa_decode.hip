@@ -378,14 +378,17 @@ __device__ __forceinline__ WaveCtx make_wave_ctx(const DecodeParams &p, int kh) 
 // The nr rounds of one chunk [tok0, tok_end) of a wave (its table entries are
 // in c.tabv), through two register buffers: at the top of the loop only A
 // (round r) is in flight.
-template <bool BS8, int DT, int D, int G, int NT>
+// With PRELOADED, round 0 is already in flight in A (issued before the
+// segment's query staging).
+template <bool BS8, bool PRELOADED, int DT, int D, int G, int NT>
 __device__ __forceinline__ void stream_rounds(const WaveCtx &c, SoftState<DT, D, G, NT> &st,
                                               const u32x4 (*qb)[D * 4 / 16], const NewRow &new_row,
-                                              float sl2, int tok0, int tok_end, int nr) {
+                                              float sl2, int tok0, int tok_end, int nr,
+                                              RoundBuf<DT, D, G, NT> &A) {
   using S = DecodeShape<DT, D, G, NT>;
   auto rtok_of = [&](int r) { return tok0 + r * S::ROUND; };
-  RoundBuf<DT, D, G, NT> A, B;
-  load_round<BS8>(A, c, rtok_of(0));
+  RoundBuf<DT, D, G, NT> B;
+  if (!PRELOADED) load_round<BS8>(A, c, rtok_of(0));
   int r = 0;
   while (r + 2 < nr) {
     load_round<BS8>(B, c, rtok_of(r + 1));
@@ -460,32 +463,49 @@ __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int 
 
   const int seg_tiles = (p_end - p_start + 15) >> 4;
   constexpr int kWin = kWaves * chunk_tiles<BS8>();
-  // The table entries of this wave's part of the first window are requested
-  // before the query rows are staged, so the two loads overlap.
-  int tab_first;
+
+  // Start-up of a segment: the group's query rows (MFMA operand B, lane l:
+  // query head (l % 16) % G, chunk (l / 16) + 4 s, read from LDS), for the
+  // decode step this KV head's new row, and the table entries of this wave's
+  // part of the first window are requested together. The rows go to LDS as
+  // they arrive; once the table entries are in, the first round of K/V loads
+  // is issued, and only then does the workgroup synchronise, so the first K/V
+  // bytes are on their way during the barrier. (The rows are written before
+  // the round is issued so that their registers are free by then.)
+  int w_t0, w_t1, tok0, tok_end;
   {
     const int win = min(kWin, seg_tiles);
-    const int tok0 = p_start + 16 * (wave * win / kWaves);
-    tab_first = table_row[min((tok0 >> c.bshift) + lane, p.max_blocks_per_seq - 1)];
+    w_t0 = wave * win / kWaves;
+    w_t1 = (wave + 1) * win / kWaves;
+    tok0 = p_start + 16 * w_t0;
+    tok_end = min(p_start + 16 * w_t1, p_end);
   }
-
-  // MFMA operand B (lane l: query head (l % 16) % G, chunk (l / 16) + 4 s) is
-  // read from LDS: the group's query rows are staged there once per segment.
+  const int tid = threadIdx.x;
+  constexpr int kQChunks = G * (S::ROWB / 16);  // <= 256: one per thread
+  static_assert(kQChunks <= kThreads, "one query chunk per thread");
   {
-    const int tid = threadIdx.x;
+    u32x4 qv = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
     const char *qrow0 = reinterpret_cast<const char *>(p.q) + ((int64_t)seq * num_q_heads + kh * G) * S::ROWB;
-    for (int i = tid; i < G * (S::ROWB / 16); i += kThreads) {
-      const int h = i / (S::ROWB / 16), ch = i % (S::ROWB / 16);
-      lds.q[h][ch] = load_chunk(qrow0, (int64_t)h * S::ROWB + ch * 16);
-    }
-    if (new_pos >= 0 && tid < 2 * (S::ROWB / 16)) {  // decode step: stage the new row
-      const int ch = tid % (S::ROWB / 16);
+    if (tid < kQChunks) qv = load_chunk(qrow0, (int64_t)(tid / (S::ROWB / 16)) * S::ROWB + (tid % (S::ROWB / 16)) * 16);
+    const bool new_thread = new_pos >= 0 && tid < 2 * (S::ROWB / 16);
+    const int ch = tid % (S::ROWB / 16);
+    if (new_thread) {  // decode step: the new row
       const int64_t src = ((int64_t)seq * p.num_kv_heads + kh) * S::ROWB + ch * 16;
-      if (tid < S::ROWB / 16) lds.newk[ch] = load_chunk(p.new_key, src);
-      else lds.newv[ch] = load_chunk(p.new_value, src);
+      nv = load_chunk(tid < S::ROWB / 16 ? p.new_key : p.new_value, src);
     }
-    __syncthreads();
+    c.first_blk = tok0 >> c.bshift;
+    c.tabv = table_row[min(c.first_blk + lane, p.max_blocks_per_seq - 1)];
+    if (tid < kQChunks) lds.q[tid / (S::ROWB / 16)][tid % (S::ROWB / 16)] = qv;
+    if (new_thread) {
+      if (tid < S::ROWB / 16) lds.newk[ch] = nv;
+      else lds.newv[ch] = nv;
+    }
   }
+  c.tabv = min(max(c.tabv, 0), p.num_blocks - 1);  // never address outside the pool
+  RoundBuf<DT, D, G, NT> A;
+  const bool first_issued = w_t0 < w_t1;
+  if (first_issued) load_round<BS8>(A, c, tok0);
+  __syncthreads();
   const NewRow new_row{new_pos, lds.newk, lds.newv};
   const u32x4 (*qb)[D * 4 / 16] = lds.q;
 
@@ -500,20 +520,20 @@ __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int 
       for (int e = 0; e < S::EPC; ++e) st.acc[h][sg][e] = 0.0f;
 
   const float sl2 = p.scale_log2;
-  for (int w0 = 0; w0 < seg_tiles; w0 += kWin) {
+  if (first_issued)
+    stream_rounds<BS8, true>(c, st, qb, new_row, sl2, tok0, tok_end,
+                             (w_t1 - w_t0 + NT - 1) / NT, A);
+  for (int w0 = kWin; w0 < seg_tiles; w0 += kWin) {
     const int win = min(kWin, seg_tiles - w0);
     const int t0 = w0 + wave * win / kWaves;
     const int t1 = w0 + (wave + 1) * win / kWaves;
     if (t0 >= t1) continue;
-    const int tok0 = p_start + 16 * t0;
-    const int tok_end = min(p_start + 16 * t1, p_end);
-    c.first_blk = tok0 >> c.bshift;
-    {
-      int raw = tab_first;
-      if (w0 > 0) raw = table_row[min(c.first_blk + lane, p.max_blocks_per_seq - 1)];
-      c.tabv = min(max(raw, 0), p.num_blocks - 1);  // never address outside the pool
-    }
-    stream_rounds<BS8>(c, st, qb, new_row, sl2, tok0, tok_end, (t1 - t0 + NT - 1) / NT);
+    const int wtok0 = p_start + 16 * t0;
+    const int wtok_end = min(p_start + 16 * t1, p_end);
+    c.first_blk = wtok0 >> c.bshift;
+    c.tabv = min(max(table_row[min(c.first_blk + lane, p.max_blocks_per_seq - 1)], 0),
+                 p.num_blocks - 1);
+    stream_rounds<BS8, false>(c, st, qb, new_row, sl2, wtok0, wtok_end, (t1 - t0 + NT - 1) / NT, A);
   }
 
   float mw[G], lw[G];
@@ -649,6 +669,16 @@ __device__ __forceinline__ float fetch(const float *p) {
 }
 
 __device__ __forceinline__ int uniform_i32(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// The equal cut of `total` units over `nwg` ranges with 32-bit arithmetic (a
+// 64-bit division is a long instruction sequence here, on every workgroup's
+// start-up path): with total = q nwg + r, floor(w total / nwg) = w q +
+// floor(w r / nwg), and w r < nwg^2 fits.
+__device__ __forceinline__ int cut_lo(int w, int total, int nwg) {
+  const int q = total / nwg;
+  const int r = total - q * nwg;
+  return w * q + (w * r) / nwg;
+}
 
 // Coordinates of the segment of a range [.., end) that starts at unit pos,
 // inside sequence seq: KV head kh, its tiles [a, b) (b <= a: the range ends in
@@ -791,8 +821,8 @@ void decode_flat_kernel(DecodeParams p) {
   extern __shared__ int s_plan[];  // tiles prefix [S + 1], clamped lengths [S], slots [S]
   __shared__ MergeLds<G, D> lds;
   __shared__ int s_wsum[kWaves];
-  __shared__ int s_found;
   __shared__ int s_last;
+  __shared__ int s_found;
 
   const int S = p.num_seqs;
   const int hkv = p.num_kv_heads;
@@ -855,18 +885,17 @@ void decode_flat_kernel(DecodeParams p) {
       for (int i = tid; i < num_q_heads * D; i += kThreads)
         out[(int64_t)s * num_q_heads * D + i] = Store<DT>::cvt(0.0f);
 
-  // Ranges of sz = ceil(total / grid) units; the last takes what is left and
-  // workgroups past it take none, so every range that exists is non-empty
-  // (the piece count of the combine counts on that). Range of unit x: x / sz.
+  // Workgroup w takes units [floor(w T / nwg), floor((w + 1) T / nwg)); with
+  // fewer units than workgroups only the first `total` take part, so every
+  // range is non-empty (the piece count of the combine counts on that). The
+  // range holding unit x is floor(((x + 1) nwg - 1) / T).
   const int nwg = min((int)gridDim.x, total);
   if (w >= nwg) {
     if (STEP) copy_new_rows<DT, D, G>(p, w + gridDim.x);
     return;
   }
-  const int start = (int)((int64_t)w * total / nwg);
-  const int end = (int)((int64_t)(w + 1) * total / nwg);
-
-  // The sequence holding unit `start`.
+  const int start = cut_lo(w, total, nwg);
+  const int end = cut_lo(w + 1, total, nwg);
   for (int s = tid; s < S; s += kThreads)
     if (hkv * s_tc[s] <= start && start < hkv * s_tc[s + 1]) s_found = s;
   __syncthreads();
