@@ -371,20 +371,23 @@ void prefill_kernel(PrefillParams p) {
       // only raised when a row's tile maximum exceeds it by more than
       // kRescaleSlack (log2 units): weights then stay below 2^kRescaleSlack,
       // well inside fp16/bf16 range, and the rescale of the accumulators (a
-      // branch uniform across the wave) is rare after the first tile.
-      float tmax[QB];
+      // branch uniform across the wave) is rare after the first tile. Each
+      // lane tests its own 8 scores; only the branch takes the row maxima
+      // across lanes.
       bool raise = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         float mx = fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), fmaxf(s[qb][0][2], s[qb][0][3]));
         mx = fmaxf(mx, fmaxf(fmaxf(s[qb][1][0], s[qb][1][1]), fmaxf(s[qb][1][2], s[qb][1][3])));
-        tmax[qb] = group_max(mx) * p.scale_log2;
-        raise |= tmax[qb] > m[qb] + kRescaleSlack;
+        raise |= fmaf(mx, p.scale_log2, -m[qb]) > kRescaleSlack;
       }
       if (__any(raise)) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          const float m_new = fmaxf(m[qb], tmax[qb]);
+          // the lane's maximum again, in another order (nothing held across the test)
+          float mx = fmaxf(fmaxf(s[qb][0][0], s[qb][1][0]), fmaxf(s[qb][0][1], s[qb][1][1]));
+          mx = fmaxf(mx, fmaxf(fmaxf(s[qb][0][2], s[qb][1][2]), fmaxf(s[qb][0][3], s[qb][1][3])));
+          const float m_new = fmaxf(m[qb], group_max(mx) * p.scale_log2);
           const float alpha = fast_exp2(m[qb] - m_new);
           m[qb] = m_new;
           lsum[qb] *= alpha;
@@ -431,11 +434,15 @@ void prefill_kernel(PrefillParams p) {
     }
   }
 
-  // out = acc / l for the valid rows.
+  // out = acc / l for the valid rows. The row index is rebuilt from an
+  // opaque copy of the lane so that no address of this store is computed
+  // before the loop and held in registers across it.
+  int lr_out = lr;
+  asm volatile("" : "+v"(lr_out));
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float inv = 1.f / lsum[qb][0];
-    const int r = qt * S::ROWS + (wave * QB + qb) * 16 + lr;
+    const int r = qt * S::ROWS + (wave * QB + qb) * 16 + lr_out;
     const int t = r / G;
     if (t >= L) continue;
     const int h = kh * G + r % G;
