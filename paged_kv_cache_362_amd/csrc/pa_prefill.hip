@@ -188,16 +188,17 @@ template <int D> struct Stager {
 
   __device__ void load_table(KVStage<D> &r, int j) const {
 #pragma unroll
-    for (int u = 0; u < S::KCH_T; ++u) {
-      // never address outside the pool, whatever the table holds
-      const int e = table[pos_of(j, key[u]) >> bshift];
-      r.phys[u] = min(uint32_t(max(e, 0)), max_block);
-    }
+    for (int u = 0; u < S::KCH_T; ++u) r.phys[u] = uint32_t(table[pos_of(j, key[u]) >> bshift]);
   }
   __device__ void load_kv(KVStage<D> &r, int j) const {
 #pragma unroll
     for (int u = 0; u < S::KCH_T; ++u) {
-      const uint64_t off = uint64_t(r.phys[u]) * blk_bytes + ((pos_of(j, key[u]) & bmask) * (D * 2) + col[u]);
+      // Never address outside the pool, whatever the table holds. The entry
+      // is clamped here, at its use one tile after its load, not in
+      // load_table: there the clamp would make the wave wait for the table
+      // load (and every K/V load issued before it) within the same tile.
+      const uint32_t phys = min(uint32_t(max(int(r.phys[u]), 0)), max_block);
+      const uint64_t off = uint64_t(phys) * blk_bytes + ((pos_of(j, key[u]) & bmask) * (D * 2) + col[u]);
       r.k[u] = *reinterpret_cast<const u32x4 *>(kbase + off);
       r.v[u] = *reinterpret_cast<const u32x4 *>(vbase + off);
     }
@@ -331,8 +332,18 @@ void prefill_kernel(PrefillParams p) {
       const int j = j0 + u;
       KVStage<D> &mine = R[u];                  // free: gets tile j + NSET
       KVStage<D> &next = R[(u + 1) % NSET];     // tile j + 1, in flight
-      st.load_kv(mine, min(j + NSET, last));
-      st.load_table(next, min(j + NSET + 1, last));
+      // At head_dim 128 the table entries of tile j + NSET + 1 are requested
+      // before the K/V of tile j + NSET, so that waiting for them (next
+      // iteration) does not wait for these K/V loads too (loads complete in
+      // order): 241 -> 225 us on a 4096-token LLaMA-7B-layer prompt. At 64
+      // the K/V first measured faster (411 vs 429 us on [1, 32, 8192, 64]).
+      if (D == 128) {
+        st.load_table(next, min(j + NSET + 1, last));
+        st.load_kv(mine, min(j + NSET, last));
+      } else {
+        st.load_kv(mine, min(j + NSET, last));
+        st.load_table(next, min(j + NSET + 1, last));
+      }
       const bool live = j < ntiles;
       const char *kb_lds = lds + u * S::BUF;
       const char *vt_lds = kb_lds + S::KBYTES;
