@@ -11,15 +11,12 @@
 // Work: one workgroup (4 waves) per (sequence, KV head, tile of kPrefillRows
 // query rows); a query row is a (token, query head of the group) pair, so the
 // G heads that share a KV head share every K/V byte. Each wave owns 2 blocks
-// of 16 rows. The keys are walked in tiles of 32 (any block size divides or is
-// a multiple of... the tile is assembled key by key through the table, so
-// block sizes 8-64 all work), double-buffered in LDS:
-//
-//   * K tile [32 keys][D] row-major (rows padded by 16 bytes).
-//   * V tile transposed, [D][32 keys], so that a lane's MFMA operand (8
-//     consecutive keys of one dim) is one 16-byte LDS read. The keys are
-//     stored permuted (see v_slot) so that those 8 keys are exactly the 8
-//     score values the same lane holds after the score product.
+// of 16 rows. The keys are walked in tiles of 32, assembled key by key
+// through the table (so block sizes 8-64 all work), double-buffered in LDS as
+// a K tile and a V tile, both [32 keys][D] row-major with rows padded by 16
+// bytes. The V operand of the second product (8 keys of one dim per lane, the
+// keys whose scores that lane holds) is read from the row-major V tile by
+// gfx950's transposing LDS read, so V is staged exactly as K is.
 //
 // Products, all on v_mfma_f32_16x16x32_{f16,bf16} with fp32 accumulation:
 //   S^T [16 keys x 16 rows] = K [keys x D] . Q^T [D x rows]     (2 key blocks)
@@ -51,23 +48,14 @@ template <int D, int QB> struct PfShape {
   static constexpr int KS = D / 32;                      // k-steps of the score product
   static constexpr int DB = D / 16;                      // 16-dim blocks of the output
   static constexpr int ROWS = kPfWaves * QB * 16;        // query rows per workgroup
-  static constexpr int KPITCH = D * 2 + 16;              // bytes per K row in LDS
-  static constexpr int VPITCH = kTileKeys * 2;           // bytes per V^T row in LDS
+  static constexpr int KPITCH = D * 2 + 16;              // bytes per K or V row in LDS
   static constexpr int KBYTES = kTileKeys * KPITCH;
-  static constexpr int BUF = KBYTES + D * VPITCH;        // one stage
+  static constexpr int BUF = 2 * KBYTES;                 // one stage: K tile, V tile
   static constexpr int DCH = D / 8;                      // 16-byte chunks per row
   static constexpr int KCH_T = kTileKeys * DCH / kPfThreads;        // (key, column) items per thread
   static_assert(kTileKeys * DCH % kPfThreads == 0, "K chunks must divide over the threads");
   static_assert(ROWS == kPrefillRows, "tile rows and host constant disagree");
 };
-
-// LDS position (0..31) of key k of a tile in the transposed V tile. Key
-// 16*blk + 4*g + i (blk < 2, g < 4, i < 4) goes to 8*g + 4*blk + i: lane group
-// g of a wave then reads keys {4g..4g+3, 16+4g..16+4g+3}, the keys whose
-// scores it holds (result rows 4g+j of both 16-key score blocks).
-__device__ __forceinline__ int v_slot(int k) {
-  return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
-}
 
 template <int DT> __device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, f32x4 c);
 template <> __device__ __forceinline__ f32x4 mfma16<PA_F16>(const u32x4 &a, const u32x4 &b, f32x4 c) {
@@ -135,6 +123,17 @@ __device__ __forceinline__ float group_max(float v) {
   return fmaxf(a, b);
 }
 
+// Transposing LDS read of 4 16-bit elements (ds_read_b64_tr_b16): within each
+// group of 16 lanes, lane c receives as its element r the element c % 4 of the
+// 8 bytes addressed by lane 4 r + c / 4 of the group.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const char *p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  typedef __attribute__((address_space(3))) char lds_char;
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)((lds_char *)p));
+  return __builtin_bit_cast(uint2, r);
+}
+
 // One stage of the global -> LDS pipeline: the table entries and the K/V
 // chunks of one key tile, held in registers by every thread.
 template <int D> struct KVStage {
@@ -143,18 +142,11 @@ template <int D> struct KVStage {
   u32x4 k[S::KCH_T], v[S::KCH_T];
 };
 
-// Value of v in lane l ^ 1 (DPP quad_perm [1, 0, 3, 2]).
-__device__ __forceinline__ uint32_t lane_pair(uint32_t v) {
-  return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0xB1, 0xF, 0xF, false));
-}
-
 // What each thread stages of a key tile, and how. Thread item p (p = tid +
 // 256 u) is key p % 32, 16-byte column p / 32, of both K and V: one table
-// entry and one address per item. Keys vary fastest across lanes, so the
-// transposed V stores of a wave spread over the LDS banks, and the two keys of
-// an (even, odd) pair sit in lanes l and l ^ 1; for the transposed V tile they
-// swap two dwords so that each lane writes 4 of the pair's 8 (key, key+1)
-// dwords.
+// entry and one address per item, and one 16-byte LDS store per tile. Keys
+// vary fastest across lanes, so with the padded rows a wave's stores spread
+// over the LDS banks.
 template <int D> struct Stager {
   using S = PfShape<D, 2>;
   const char *kbase;     // k_cache + kh * B * D elements, in bytes
@@ -165,8 +157,7 @@ template <int D> struct Stager {
   uint32_t bshift, bmask;
   uint32_t last_pos;     // context length - 1
   uint32_t key[S::KCH_T], col[S::KCH_T];  // item's key in the tile and byte column
-  uint32_t klds[S::KCH_T], vlds[S::KCH_T];
-  bool odd[S::KCH_T];
+  uint32_t klds[S::KCH_T];
 
   __device__ void init(int tid) {
 #pragma unroll
@@ -176,8 +167,6 @@ template <int D> struct Stager {
       const int c = p / kTileKeys;
       col[u] = c * 16;
       klds[u] = key[u] * S::KPITCH + col[u];
-      odd[u] = key[u] & 1;
-      vlds[u] = S::KBYTES + v_slot(key[u] & ~1u) * 2 + (8 * c + 4 * (key[u] & 1)) * S::VPITCH;
     }
   }
   // Position of key `k` of tile j, clamped to the last cached position: keys
@@ -207,19 +196,7 @@ template <int D> struct Stager {
 #pragma unroll
     for (int u = 0; u < S::KCH_T; ++u) {
       *reinterpret_cast<u32x4 *>(buf + klds[u]) = r.k[u];
-      // Even key: keeps dims 0-3 of the column (own words 0, 1) and receives
-      // the odd key's; odd key: keeps dims 4-7 (own words 2, 3), receives the
-      // even key's.
-      const uint32_t o0 = r.v[u][0], o1 = r.v[u][1], o2 = r.v[u][2], o3 = r.v[u][3];
-      const uint32_t r0 = lane_pair(odd[u] ? o0 : o2);
-      const uint32_t r1 = lane_pair(odd[u] ? o1 : o3);
-      const uint32_t lo0 = odd[u] ? r0 : o0, lo1 = odd[u] ? r1 : o1;  // the even key's words
-      const uint32_t hi0 = odd[u] ? o2 : r0, hi1 = odd[u] ? o3 : r1;  // the odd key's words
-      char *dst = buf + vlds[u];
-      *reinterpret_cast<uint32_t *>(dst) = __builtin_amdgcn_perm(hi0, lo0, 0x05040100u);
-      *reinterpret_cast<uint32_t *>(dst + S::VPITCH) = __builtin_amdgcn_perm(hi0, lo0, 0x07060302u);
-      *reinterpret_cast<uint32_t *>(dst + 2 * S::VPITCH) = __builtin_amdgcn_perm(hi1, lo1, 0x05040100u);
-      *reinterpret_cast<uint32_t *>(dst + 3 * S::VPITCH) = __builtin_amdgcn_perm(hi1, lo1, 0x07060302u);
+      *reinterpret_cast<u32x4 *>(buf + S::KBYTES + klds[u]) = r.v[u];
     }
   }
 };
@@ -332,18 +309,11 @@ void prefill_kernel(PrefillParams p) {
       const int j = j0 + u;
       KVStage<D> &mine = R[u];                  // free: gets tile j + NSET
       KVStage<D> &next = R[(u + 1) % NSET];     // tile j + 1, in flight
-      // At head_dim 128 the table entries of tile j + NSET + 1 are requested
-      // before the K/V of tile j + NSET, so that waiting for them (next
-      // iteration) does not wait for these K/V loads too (loads complete in
-      // order): 241 -> 225 us on a 4096-token LLaMA-7B-layer prompt. At 64
-      // the K/V first measured faster (411 vs 429 us on [1, 32, 8192, 64]).
-      if (D == 128) {
-        st.load_table(next, min(j + NSET + 1, last));
-        st.load_kv(mine, min(j + NSET, last));
-      } else {
-        st.load_kv(mine, min(j + NSET, last));
-        st.load_table(next, min(j + NSET + 1, last));
-      }
+      // The table entries of tile j + NSET + 1 are requested before the K/V
+      // of tile j + NSET, so that waiting for them (next iteration) does not
+      // wait for these K/V loads too: loads complete in order.
+      st.load_table(next, min(j + NSET + 1, last));
+      st.load_kv(mine, min(j + NSET, last));
       const bool live = j < ntiles;
       const char *kb_lds = lds + u * S::BUF;
       const char *vt_lds = kb_lds + S::KBYTES;
@@ -424,15 +394,22 @@ void prefill_kernel(PrefillParams p) {
         }
       }
 
-      // O^T += V^T . P^T, and the row sums.
+      // O^T += V^T . P^T, and the row sums. A lane's V^T operand is dim
+      // 16 db + lr of the 8 keys whose weights it holds (keys 4 lg .. 4 lg + 3
+      // and 16 + 4 lg .. 16 + 4 lg + 3 of the tile, in that order), built from
+      // the row-major V tile by two transposing reads: lane (lr, lg) addresses
+      // key 4 lg + lr / 4 (then that key + 16), dims 16 db + 4 (lr % 4) .. + 3.
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         lsum[qb] = mfma16<DT>(ones, ph[qb], lsum[qb]);
         if (DT == PA_BF16) lsum[qb] = mfma16<DT>(ones, pl[qb], lsum[qb]);
       }
+      const char *vt_lane = vt_lds + (4 * lg + (lr >> 2)) * S::KPITCH + (lr & 3) * 8;
 #pragma unroll
       for (int db = 0; db < S::DB; ++db) {
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(vt_lds + (16 * db + lr) * S::VPITCH + 16 * lg);
+        const uint2 lo = lds_read_tr16(vt_lane + 32 * db);
+        const uint2 hi = lds_read_tr16(vt_lane + 32 * db + 16 * S::KPITCH);
+        const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           acc[qb][db] = mfma16<DT>(a, ph[qb], acc[qb][db]);
