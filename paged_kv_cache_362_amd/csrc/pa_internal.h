@@ -19,11 +19,14 @@ constexpr int kDefaultPartition = 256;
 constexpr int kMaxPlanSeqs = 4096;
 constexpr int kMaxFlatWorkgroups = 2048;
 // Resident balanced-form workgroups per compute unit, at most. Measured on
-// MI355X: 3 beats the 4 that fit at 4 waves per SIMD (LLaMA-7B decode step
-// 101.6 -> 101.0 us, 13B 109.6 -> 107.7 us, three runs each): 12 waves per CU
-// keep ~190 KB of loads in flight, far above what the HBM latency needs, and
-// the longer ranges cut split pieces; 2 is slower.
-constexpr int kMaxFlatWgsPerCu = 3;
+// MI355X (fused decode step, two interleaved runs, 3 -> 2 per CU): LLaMA-7B
+// layer 99.9 -> 98.7 us, GQA bf16 87.4 -> 86.2 us, LLaMA-13B layer with a
+// shared prefix 107.4 -> 102.6 us, the 67 MB long context unchanged. Eight
+// waves per CU still keep ~128 KB of loads in flight, the longer ranges cut
+// split pieces, and fewer co-resident workgroups narrow the spread of the
+// compute units' finishing times. One per CU is slower except on the shared
+// prefix (101.5 us). 4 per CU was slower than 3.
+constexpr int kMaxFlatWgsPerCu = 2;
 
 struct DecodeParams {
   void *out;
