@@ -256,7 +256,8 @@ void prefill_kernel(PrefillParams p) {
       qreg[qb][ks] = valid ? v : u32x4{0, 0, 0, 0};
     }
   }
-  const int wave_min_qpos = n - L + (qt * S::ROWS + wave * QB * 16) / G;
+  const int wave_min_qpos =
+      __builtin_amdgcn_readfirstlane(n - L + (qt * S::ROWS + wave * QB * 16) / G);
   const int r_last = min(rows, (qt + 1) * S::ROWS) - 1;
   const int last_pos = n - L + r_last / G;
   const int ntiles = last_pos / kTileKeys + 1;
@@ -276,10 +277,10 @@ void prefill_kernel(PrefillParams p) {
   // V^T rows are all ones (the MFMA sums the weights it is given, so the
   // denominator uses exactly the rounded weights the numerator does).
   f32x4 acc[QB][S::DB], lsum[QB];
-  float m[QB];
+  float nm[QB];  // minus the running maximum (log2 domain), as the exponent FMA takes it
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY;
+    nm[qb] = INFINITY;
     lsum[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < S::DB; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -360,7 +361,7 @@ void prefill_kernel(PrefillParams p) {
       for (int qb = 0; qb < QB; ++qb) {
         float mx = fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), fmaxf(s[qb][0][2], s[qb][0][3]));
         mx = fmaxf(mx, fmaxf(fmaxf(s[qb][1][0], s[qb][1][1]), fmaxf(s[qb][1][2], s[qb][1][3])));
-        raise |= fmaf(mx, p.scale_log2, -m[qb]) > kRescaleSlack;
+        raise |= fmaf(mx, p.scale_log2, nm[qb]) > kRescaleSlack;
       }
       if (__any(raise)) {
 #pragma unroll
@@ -368,9 +369,9 @@ void prefill_kernel(PrefillParams p) {
           // the lane's maximum again, in another order (nothing held across the test)
           float mx = fmaxf(fmaxf(s[qb][0][0], s[qb][1][0]), fmaxf(s[qb][0][1], s[qb][1][1]));
           mx = fmaxf(mx, fmaxf(fmaxf(s[qb][0][2], s[qb][1][2]), fmaxf(s[qb][0][3], s[qb][1][3])));
-          const float m_new = fmaxf(m[qb], group_max(mx) * p.scale_log2);
-          const float alpha = fast_exp2(m[qb] - m_new);
-          m[qb] = m_new;
+          const float m_new = fmaxf(-nm[qb], group_max(mx) * p.scale_log2);
+          const float alpha = fast_exp2(-nm[qb] - m_new);
+          nm[qb] = -m_new;
           lsum[qb] *= alpha;
 #pragma unroll
           for (int db = 0; db < S::DB; ++db) acc[qb][db] *= alpha;
@@ -384,7 +385,7 @@ void prefill_kernel(PrefillParams p) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
-            e[4 * kb + jj] = fast_exp2(fmaf(s[qb][kb][jj], p.scale_log2, -m[qb]));
+            e[4 * kb + jj] = fast_exp2(fmaf(s[qb][kb][jj], p.scale_log2, nm[qb]));
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const uint32_t hw = cvt2<DT>(e[2 * w], e[2 * w + 1]);
