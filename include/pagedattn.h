@@ -177,17 +177,20 @@ int32_t pa_decode(void *out, const void *q, const void *k_cache,
  * slot_mapping, num_seqs, ...) followed by pa_decode(..., partition_size = 0,
  * ...): the pools end with the new rows in place and `out` is bit-identical.
  * Token s of key/value [num_seqs, num_kv_heads, head_dim] belongs to sequence
- * s and must be its last attended position: for context_lens[s] >= 1 and
- * slot_mapping[s] >= 0, slot_mapping[s] must be the slot of position
- * context_lens[s] - 1 (table entry (n-1)/block_size, offset (n-1)%block_size),
- * checked under PA_DEBUG only. slot_mapping[s] < 0 writes nothing for that
- * sequence (its last position is then read from the pools).
+ * s. Normally it is the sequence's last attended position: slot_mapping[s] is
+ * the slot of position context_lens[s] - 1 (table entry (n-1)/block_size,
+ * offset (n-1)%block_size), and the attention then reads that position's K/V
+ * from key/value, not from the pool, so the write and the reads need no
+ * ordering inside the launch. A token may also be written to a slot that no
+ * sequence of the call attends (a fresh block past the context): the row is
+ * written and not read. Any other slot (an attended position of another
+ * sequence, or of its own other than the last) breaks the call's
+ * preconditions; checked under PA_DEBUG only. slot_mapping[s] < 0 writes
+ * nothing for that sequence (its last position is then read from the pools).
  *
- * The attention reads the new rows from key/value, not from the pools, so the
- * write and the reads need no ordering inside the launch. Workspace as for
- * pa_decode with partition_size 0 (zero-filled before its first use). Beyond
- * 4096 sequences the call writes first and then decodes with fixed partitions
- * (two launches).
+ * Workspace as for pa_decode with partition_size 0 (zero-filled before its
+ * first use). Beyond 4096 sequences the call writes first and then decodes
+ * with fixed partitions (two launches).
  */
 int32_t pa_decode_step(void *out, const void *q, const void *key,
                        const void *value, void *k_cache, void *v_cache,

@@ -516,21 +516,35 @@ int32_t decode_impl(void *out, const void *q, const void *k_cache, const void *v
         if (b < 0 || b >= num_blocks) return PA_ERR_BAD_INDEX;
       }
     }
-    if (fused) {  // each new token is the last position of its sequence
+    if (fused) {
+      // Each written slot is either its own sequence's last attended position
+      // or a slot no sequence attends: the launch reads no other slot it writes.
       std::vector<int32_t> slots(num_seqs);
       st = sync_copy_to_host(slots.data(), step.slot_mapping, sizeof(int32_t) * slots.size(), s);
       if (st != PA_OK) return st;
       std::unordered_set<int32_t> seen;
+      bool any_elsewhere = false;
       for (int32_t i = 0; i < num_seqs; ++i) {
         const int32_t v = slots[i];
         if (v < 0) continue;
         if (v >= num_slots || !seen.insert(v).second) return PA_ERR_BAD_INDEX;
         const int32_t n = lens[i];
-        if (n < 1) continue;
-        const int32_t last = n - 1;
-        const int32_t want = tab[size_t(i) * max_blocks_per_seq + last / block_size] * block_size +
-                             last % block_size;
-        if (v != want) return PA_ERR_BAD_INDEX;
+        bool last_pos = false;
+        if (n >= 1) {
+          const int32_t last = n - 1;
+          last_pos = v == tab[size_t(i) * max_blocks_per_seq + last / block_size] * block_size +
+                              last % block_size;
+        }
+        any_elsewhere |= !last_pos;
+      }
+      if (any_elsewhere) {
+        for (int32_t i = 0; i < num_seqs; ++i)
+          for (int32_t t = 0; t < lens[i]; ++t) {
+            const int32_t slot =
+                tab[size_t(i) * max_blocks_per_seq + t / block_size] * block_size + t % block_size;
+            const bool own_last = t == lens[i] - 1 && slots[i] == slot;
+            if (!own_last && seen.count(slot)) return PA_ERR_BAD_INDEX;
+          }
       }
     }
     if (balanced && !step.static_scratch) {  // the arrival counters must be zero

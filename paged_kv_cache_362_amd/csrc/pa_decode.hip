@@ -219,7 +219,7 @@ template <int DT, int D, int G, int NT> struct SoftState {
 
 // The row of the token written in this decode step, staged in LDS.
 struct NewRow {
-  int pos;            // its position in the sequence, or -1 when there is none
+  int pos;            // its position in the sequence, or -1 when the chunk holds none
   const u32x4 *k;     // 16-byte chunks of its K row (this KV head)
   const u32x4 *v;
 };
@@ -351,6 +351,7 @@ template <int G, int D> struct MergeLds {
   u32x4 q[G][D * 4 / 16];  // the group's query rows in 16-byte chunks (room for f32 rows)
   u32x4 newk[D * 4 / 16];  // decode step: this KV head's row of the token written this step
   u32x4 newv[D * 4 / 16];
+  int new_slot;            // decode step: the slot that row is written to
 };
 
 // Tiles of a wave's chunk inside one window: at most 64 blocks of table.
@@ -453,7 +454,7 @@ __device__ __forceinline__ void merge_token_groups(SoftState<DT, D, G, NT> &st, 
 template <int DT, int D, int G, int NT, bool BS8>
 __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int kh, int p_start,
                                             int p_end, int wave, MergeLds<G, D> &lds,
-                                            int new_pos = -1) {
+                                            int new_pos = -1, int new_slot = -1) {
   using S = DecodeShape<DT, D, G, NT>;
   const int lane = __lane_id();
   const int num_q_heads = p.num_kv_heads * G;
@@ -499,6 +500,7 @@ __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int 
     if (new_thread) {
       if (tid < S::ROWB / 16) lds.newk[ch] = nv;
       else lds.newv[ch] = nv;
+      if (tid == 0) lds.new_slot = new_slot;
     }
   }
   c.tabv = min(max(c.tabv, 0), p.num_blocks - 1);  // never address outside the pool
@@ -506,7 +508,17 @@ __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int 
   const bool first_issued = w_t0 < w_t1;
   if (first_issued) load_round<BS8>(A, c, tok0);
   __syncthreads();
-  const NewRow new_row{new_pos, lds.newk, lds.newv};
+  // Decode step: the sequence's last attended position takes the staged row
+  // only if this step writes that position's slot (the row may go to a fresh
+  // block outside the context instead, where nothing in this launch reads it).
+  // The check is made per chunk, from its table entries, with scalar values.
+  auto new_pos_in = [&](int t_begin, int t_end) -> int {
+    if (new_pos < t_begin || new_pos >= t_end) return -1;
+    const int phys = __builtin_amdgcn_readlane(c.tabv, (new_pos >> c.bshift) - c.first_blk);
+    const int slot = (phys << c.bshift) + (new_pos & ((1 << c.bshift) - 1));
+    return slot == __builtin_amdgcn_readfirstlane(lds.new_slot) ? new_pos : -1;
+  };
+  NewRow new_row{new_pos_in(tok0, tok_end), lds.newk, lds.newv};
   const u32x4 (*qb)[D * 4 / 16] = lds.q;
 
   SoftState<DT, D, G, NT> st;
@@ -533,6 +545,7 @@ __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int 
     c.first_blk = wtok0 >> c.bshift;
     c.tabv = min(max(table_row[min(c.first_blk + lane, p.max_blocks_per_seq - 1)], 0),
                  p.num_blocks - 1);
+    new_row.pos = new_pos_in(wtok0, wtok_end);
     stream_rounds<BS8, false>(c, st, qb, new_row, sl2, wtok0, wtok_end, (t1 - t0 + NT - 1) / NT, A);
   }
 
@@ -908,10 +921,12 @@ void decode_flat_kernel(DecodeParams p) {
       const SegCoords c = seg_coords(s_tc, seq, hkv, cost, pos, end);
       if (c.b <= c.a) break;  // the range ends inside this pair's overhead units
       const int n = s_n[seq];
-      int new_pos = -1;  // decode step: the written position, when this segment ends the item
+      // decode step: the last attended position, when this segment ends the
+      // item (its staged row replaces the pool's if the step writes that slot)
+      int new_pos = -1;
       if (STEP && c.b == c.tiles && s_slot[seq] >= 0) new_pos = n - 1;
       run_segment<DT, D, G, NT, BS8>(p, seq, c.kh, 16 * c.a, min(16 * c.b, n), wave, lds,
-                                     new_pos);
+                                     new_pos, s_slot[seq]);
     }
     __syncthreads();
     const SegCoords c = seg_coords(s_tc, seq, hkv, cost, pos, end);

@@ -162,7 +162,8 @@ def decode_step(q: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
                 max_context_len: int, out: torch.Tensor | None = None,
                 workspace: torch.Tensor | None = None) -> torch.Tensor:
     """One decode step in one launch: write key/value [S, Hkv, D] at slot_mapping
-    [S] (each the last position of its sequence), then paged attention."""
+    [S] (each the last attended position of its sequence, or a slot no sequence
+    attends), then paged attention."""
     out, workspace = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
                                   max_context_len, out, workspace, 0)
     _on_gpu(key, value, slot_mapping)

@@ -57,8 +57,8 @@ def test_full_config_parity(cfg):
     poisoned pools, against the oracle run over the whole batch. The two
     outputs are bit-identical, the pools equal the oracle's write bit for bit,
     and a rerun of the decode reproduces its output bit for bit. (The tiny
-    workload's token goes into a fresh block outside its context; only the two
-    calls express that.)"""
+    workload's token goes into a fresh block outside its context: the fused
+    step writes that slot and reads nothing from it.)"""
     b = layouts.make_config(cfg, poison=True)
     kc, vc, o64 = oracle_step(b)
     t, out = gpu_step(b)
@@ -69,11 +69,8 @@ def test_full_config_parity(cfg):
                       t["context_lens"], b.scale, b.max_context_len)
     assert torch.equal(_bits(out), _bits(out2))
     del t
-    if not layouts.new_tokens_are_last(b):
-        # the tiny workload writes into a fresh block outside its context, which
-        # the fused step (new token = last attended position) does not express;
-        # it is timed as the two calls
-        return
+    # the fused step too; the tiny workload writes its token into a fresh block
+    # outside its context, a slot the launch writes and does not read
     t_step = layouts.to_device(b)
     out_step = ops.decode_step(t_step["q"], t_step["new_key"], t_step["new_value"],
                                t_step["k_cache"], t_step["v_cache"], t_step["slot_mapping"],
@@ -543,10 +540,39 @@ def test_decode_step_many_sequences_falls_back():
 
 
 def test_decode_step_checks_slots_in_debug_mode(monkeypatch):
+    """A token written over a position the launch also reads (here its own
+    position n - 2) breaks the step's precondition; PA_DEBUG reports it."""
     b = layouts.scaled_config(2, max_seqs=4, max_len=300)
     t = layouts.to_device(b)
-    t["slot_mapping"][2] += 1  # not the last position any more
+    n, bs = int(b.context_lens[2]), b.block_size
+    pos = n - 2
+    t["slot_mapping"][2] = int(b.block_tables[2, pos // bs]) * bs + pos % bs
     monkeypatch.setenv("PA_DEBUG", "1")
     with pytest.raises(ops.PagedAttentionError) as e:
         _fused(b, t)
     assert e.value.code == 6
+
+
+@pytest.mark.parametrize("debug", [False, True])
+def test_decode_step_writes_outside_the_context(monkeypatch, debug):
+    """A token written to a slot no sequence attends (a free block): the fused
+    step writes the row and reads the sequence's last position from the pool,
+    bit-identical to the two calls, with PA_DEBUG's check passing too."""
+    b = layouts.scaled_config(2, poison=False, max_seqs=4, max_len=300)
+    bs = b.block_size
+    used = {int(b.block_tables[s, j]) for s in range(b.num_seqs)
+            for j in range((int(b.context_lens[s]) + bs - 1) // bs)}
+    free = next(i for i in range(b.k_cache.shape[0]) if i not in used)
+    t1 = layouts.to_device(b)
+    t2 = layouts.to_device(b)
+    for t in (t1, t2):
+        t["slot_mapping"][1] = free * bs + 3
+    if debug:
+        monkeypatch.setenv("PA_DEBUG", "1")
+    o_sep = _two_calls(b, t1)
+    o_fused = _fused(b, t2)
+    torch.cuda.synchronize()
+    assert _same_bits(o_sep, o_fused)
+    assert _same_bits(t1["k_cache"], t2["k_cache"]) and _same_bits(t1["v_cache"], t2["v_cache"])
+    row = layouts.from_device(t2["k_cache"], b.dtype)[free, :, 3]
+    assert np.array_equal(row.view(np.uint8), b.new_key[1].view(np.uint8))
