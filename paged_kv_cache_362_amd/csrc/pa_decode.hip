@@ -413,6 +413,27 @@ __device__ __forceinline__ void stream_rounds(const WaveCtx &c, SoftState<DT, D,
   }
 }
 
+// Sum / maximum of v over lanes l and l ^ mask (mask 8, 16 or 32), in every
+// lane. 16 and 32 go through gfx950's row-swap permutes (v_permlane16_swap:
+// odd 16-lane rows of one operand with even rows of the other; v_permlane32_swap:
+// the upper 32 lanes of one with the lower 32 of the other), so each step is
+// two VALU operations instead of an LDS crossbar round trip; the two operands
+// then hold the pair's two values in every lane. Addition is commutative, so
+// every lane gets the same bits, and the pairs are those of a butterfly.
+template <bool MAX>
+__device__ __forceinline__ float xor_reduce(float v, int mask) {
+  if (mask == 16 || mask == 32) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto r = mask == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                              : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    const float a = __builtin_bit_cast(float, r0), b = __builtin_bit_cast(float, r1);
+    return MAX ? fmaxf(a, b) : a + b;
+  }
+  const float o = __shfl_xor(v, mask);
+  return MAX ? fmaxf(v, o) : v + o;
+}
+
 // Merge the token groups of the wave (lanes l, l ^ LPT, l ^ 2 LPT, ... hold the
 // same row chunk for different tokens). Afterwards every lane holds each
 // head's wave maximum mw and sum lw, and lanes l < LPT the head's merged
@@ -426,18 +447,18 @@ __device__ __forceinline__ void merge_token_groups(SoftState<DT, D, G, NT> &st, 
     const float mg = from_head<G>(st.m, h);
     float m = mg;
 #pragma unroll
-    for (int mask = S::LPT; mask < kWave; mask <<= 1) m = fmaxf(m, __shfl_xor(m, mask));
+    for (int mask = S::LPT; mask < kWave; mask <<= 1) m = xor_reduce<true>(m, mask);
     const float f = m == -INFINITY ? 0.0f : fast_exp2(mg - m);
     float l = from_head<G>(st.l, h) * f;
 #pragma unroll
-    for (int mask = S::LPT; mask < kWave; mask <<= 1) l += __shfl_xor(l, mask);
+    for (int mask = S::LPT; mask < kWave; mask <<= 1) l = xor_reduce<false>(l, mask);
 #pragma unroll
     for (int sg = 0; sg < S::NSEG; ++sg)
 #pragma unroll
       for (int e = 0; e < S::EPC; ++e) {
         float a = st.acc[h][sg][e] * f;
 #pragma unroll
-        for (int mask = S::LPT; mask < kWave; mask <<= 1) a += __shfl_xor(a, mask);
+        for (int mask = S::LPT; mask < kWave; mask <<= 1) a = xor_reduce<false>(a, mask);
         st.acc[h][sg][e] = a;
       }
     mw[h] = m;
