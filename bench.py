@@ -585,7 +585,7 @@ def workload_summary(cfg: int, r: dict, trace) -> dict:
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(sequences or KV heads would shard across GPUs with no exchange inside "
               f"attention, which is not built here)", file=sys.stderr)
         return 2
