@@ -884,6 +884,9 @@ void decode_flat_kernel(DecodeParams p) {
   for (int base = 0; base < S; base += kThreads) {
     const int s = base + tid;
     int n = s < S ? min(p.context_lens[s], p.max_context_len) : 0;
+    // requested with the length, not after the scan's barrier (which would add
+    // a memory round trip to every workgroup's start)
+    const int slot = STEP && s < S ? p.slot_mapping[s] : -1;
     n = max(n, 0);
     int x = (n + 15) >> 4;
     if (x > 0) x += cost;  // each (sequence, KV head) is charged `cost` tiles more
@@ -903,7 +906,6 @@ void decode_flat_kernel(DecodeParams p) {
     if (s < S) {
       s_tc[s + 1] = off + x;
       s_n[s] = n;
-      const int slot = STEP ? p.slot_mapping[s] : -1;
       s_slot[s] = slot >= 0 && slot < p.num_slots ? slot : -1;
     }
     carry += total;
