@@ -413,6 +413,22 @@ __device__ __forceinline__ void stream_rounds(const WaveCtx &c, SoftState<DT, D,
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: within each 16-lane row
+// by DPP row shifts (row_shr 1, 2, 4, 8; lanes with no source lane in the row
+// add 0), then each row adds the totals of the rows before it (lanes 15, 31,
+// 47, read as scalars). No LDS crossbar round trips.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15);
+  const int r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int lane = __lane_id();
+  return x + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+}
+
 // Sum / maximum of v over lanes l and l ^ mask (mask 8, 16 or 32), in every
 // lane. 16 and 32 go through gfx950's row-swap permutes (v_permlane16_swap:
 // odd 16-lane rows of one operand with even rows of the other; v_permlane32_swap:
@@ -890,11 +906,7 @@ void decode_flat_kernel(DecodeParams p) {
     n = max(n, 0);
     int x = (n + 15) >> 4;
     if (x > 0) x += cost;  // each (sequence, KV head) is charged `cost` tiles more
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int y = __shfl_up(x, o);
-      if (lane >= o) x += y;
-    }
+    x = wave_inclusive_scan(x);
     if (lane == kWave - 1) s_wsum[wave] = x;
     __syncthreads();
     int off = carry, total = 0;
