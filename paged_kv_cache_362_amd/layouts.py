@@ -338,9 +338,10 @@ def make_prefill_workload(name: str, seed: int = 7) -> PrefillBatch:
 
 def new_tokens_are_last(b: PagedBatch) -> bool:
     """Whether each sequence's new token is written to the slot of its last
-    attended position (context_lens[s] - 1), which the fused decode step
-    (pa_decode_step) requires. The tiny workload writes its token into a fresh
-    block outside the attended context instead."""
+    attended position (context_lens[s] - 1), where the fused decode step
+    (pa_decode_step) takes its K/V from the new rows. The tiny workload writes
+    its token into a fresh block outside the attended context instead (a slot
+    the step writes and does not read)."""
     for s, n in enumerate(b.context_lens):
         n = int(n)
         slot = int(b.slot_mapping[s])

@@ -216,9 +216,9 @@ def test_swap_needs_room_and_equal_blocks():
 
 
 def test_new_tokens_are_last_positions_except_in_the_tiny_workload():
-    """The fused decode step needs every new token at its sequence's last
-    attended position; workloads 2-5 write there, the tiny one writes into a
-    fresh block outside its 50-token context."""
+    """Workloads 2-5 write every new token at its sequence's last attended
+    position; the tiny one writes into a fresh block outside its 50-token
+    context (both forms the fused decode step covers)."""
     assert not layouts.new_tokens_are_last(layouts.make_config(1))
     for c in (2, 4):
         assert layouts.new_tokens_are_last(layouts.make_config(c))
