@@ -482,6 +482,89 @@ __device__ __forceinline__ void merge_token_groups(SoftState<DT, D, G, NT> &st, 
   }
 }
 
+// Partials shared between workgroups are written and read at agent scope:
+// written through to the device-coherent level and read from it, never from a
+// stale per-XCD L2 line.
+__device__ __forceinline__ void publish(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float fetch(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A split piece of a workgroup's range whose partials are published and whose
+// arrival is not yet counted (item -1: none).
+struct PendingPiece {
+  int item, first, last;
+};
+
+// The last piece of a split (sequence, KV head) to arrive combines the
+// partials of pieces first..last (slots item + j) in one pass with a running
+// maximum, a batch of pieces at a time. Every output element a thread owns
+// (G * D / 256 of them, or one) is handled in the same batch, so all of its
+// requests are in flight together: the partials are read at agent scope, and
+// each round trip from there costs microseconds while the memory system is
+// busy.
+template <int DT, int G, int D>
+__device__ __forceinline__ void combine_pieces(const DecodeParams &p, typename Store<DT>::T *out,
+                                               int item, int first, int last) {
+  constexpr int E = (G * D + kThreads - 1) / kThreads;  // elements per thread
+  constexpr int PB = E >= 4 ? 2 : E == 2 ? 4 : 8;        // pieces per batch: 24 requests a thread
+  int tid = threadIdx.x;
+  // Opaque to the optimiser, so these addresses are formed here rather than
+  // hoisted out of the segment loop and kept (or spilled) across it.
+  asm volatile("" : "+v"(tid));
+  float mrun[E], num[E], den[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    mrun[e] = -INFINITY;
+    num[e] = 0.0f;
+    den[e] = 0.0f;
+  }
+  for (int j0 = first; j0 <= last; j0 += PB) {
+    float mj[E][PB], lj[E][PB], aj[E][PB];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int idx = min(tid + e * kThreads, G * D - 1);
+      const int h = idx / D, d = idx % D;
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {  // `last` is uniform: no request past the last piece
+        const int64_t sl = (int64_t)item + j0 + u;
+        const bool have = j0 + u <= last;
+        mj[e][u] = have ? fetch(p.ws_m + sl * G + h) : -INFINITY;
+        lj[e][u] = have ? fetch(p.ws_l + sl * G + h) : 0.0f;
+        aj[e][u] = have ? fetch(p.ws_acc + (sl * G + h) * D + d) : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float mnew = mrun[e];
+#pragma unroll
+      for (int u = 0; u < PB; ++u)
+        if (j0 + u <= last) mnew = fmaxf(mnew, mj[e][u]);
+      const float sc = mrun[e] == -INFINITY ? 0.0f : fast_exp2(mrun[e] - mnew);
+      num[e] *= sc;
+      den[e] *= sc;
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        if (j0 + u > last) continue;
+        const float f = fast_exp2(mj[e][u] - mnew);
+        num[e] = fmaf(f, aj[e][u], num[e]);
+        den[e] = fmaf(f, lj[e][u], den[e]);
+      }
+      mrun[e] = mnew;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int idx = tid + e * kThreads;
+    if (idx < G * D) {
+      const int h = idx / D, d = idx % D;
+      out[((int64_t)item * G + h) * D + d] = Store<DT>::cvt(num[e] / den[e]);
+    }
+  }
+}
+
 // A segment [p_start, p_end) of sequence `seq`, KV head `kh`, processed by the
 // four waves. The segment is cut into windows of up to 4 * chunk_tiles tiles;
 // each wave takes a contiguous quarter of a window (a chunk that touches at
@@ -491,7 +574,8 @@ __device__ __forceinline__ void merge_token_groups(SoftState<DT, D, G, NT> &st, 
 template <int DT, int D, int G, int NT, bool BS8>
 __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int kh, int p_start,
                                             int p_end, int wave, MergeLds<G, D> &lds,
-                                            int new_pos = -1, int new_slot = -1) {
+                                            int new_pos, int new_slot, PendingPiece &pend,
+                                            int *s_pend_last) {
   using S = DecodeShape<DT, D, G, NT>;
   const int lane = __lane_id();
   const int num_q_heads = p.num_kv_heads * G;
@@ -540,11 +624,35 @@ __device__ __forceinline__ void run_segment(const DecodeParams &p, int seq, int 
       if (tid == 0) lds.new_slot = new_slot;
     }
   }
+  // The previous split piece of this range, published but not yet counted:
+  // its partials were stored before this segment's first loads, so once those
+  // have returned (and every thread has waited for its own) the piece is
+  // counted in, while this segment's first K/V round is requested; the count's
+  // round trip and the stores' completion overlap this segment's start.
+  const bool counting = pend.item >= 0;
+  if (counting) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
   c.tabv = min(max(c.tabv, 0), p.num_blocks - 1);  // never address outside the pool
+  int arrived = 0;
+  if (counting && tid == 0)
+    arrived = __hip_atomic_fetch_add(p.ws_count + pend.item, 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
   RoundBuf<DT, D, G, NT> A;
   const bool first_issued = w_t0 < w_t1;
   if (first_issued) load_round<BS8>(A, c, tok0);
+  if (counting && tid == 0) *s_pend_last = arrived == pend.last - pend.first;
   __syncthreads();
+  if (counting) {
+    if (*s_pend_last) {
+      combine_pieces<DT, G, D>(p, reinterpret_cast<typename Store<DT>::T *>(p.out), pend.item,
+                               pend.first, pend.last);
+      if (tid == 0)  // leave the counter zero for the next call
+        __hip_atomic_store(p.ws_count + pend.item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    pend.item = -1;
+  }
   // Decode step: the sequence's last attended position takes the staged row
   // only if this step writes that position's slot (the row may go to a fresh
   // block outside the context instead, where nothing in this launch reads it).
@@ -648,7 +756,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   }
   if (p_start >= n) return;
   const int p_end = min(p_start + p.partition_size, n);
-  run_segment<DT, D, G, NT, BS8>(p, seq, kh, p_start, p_end, wave, lds);
+  PendingPiece none{-1, 0, 0};
+  run_segment<DT, D, G, NT, BS8>(p, seq, kh, p_start, p_end, wave, lds, -1, -1, none, nullptr);
   __syncthreads();
 
   const bool single = n <= p.partition_size;
@@ -708,15 +817,6 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeParams p) {
 // the host takes this form only when an upper bound of the units does.
 // ---------------------------------------------------------------------------
 
-// Partials shared between workgroups are written and read at agent scope:
-// written through to the device-coherent level and read from it, never from a
-// stale per-XCD L2 line.
-__device__ __forceinline__ void publish(float *p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float fetch(const float *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 __device__ __forceinline__ int uniform_i32(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -795,73 +895,6 @@ __device__ __forceinline__ void copy_new_rows(const DecodeParams &p, int first) 
   }
 }
 
-// The last piece of a split (sequence, KV head) to arrive combines the
-// partials of pieces first..last (slots item + j) in one pass with a running
-// maximum, a batch of pieces at a time. Every output element a thread owns
-// (G * D / 256 of them, or one) is handled in the same batch, so all of its
-// requests are in flight together: the partials are read at agent scope, and
-// each round trip from there costs microseconds while the memory system is
-// busy.
-template <int DT, int G, int D>
-__device__ __forceinline__ void combine_pieces(const DecodeParams &p, typename Store<DT>::T *out,
-                                               int item, int first, int last) {
-  constexpr int E = (G * D + kThreads - 1) / kThreads;  // elements per thread
-  constexpr int PB = E >= 4 ? 2 : E == 2 ? 4 : 8;        // pieces per batch: 24 requests a thread
-  int tid = threadIdx.x;
-  // Opaque to the optimiser, so these addresses are formed here rather than
-  // hoisted out of the segment loop and kept (or spilled) across it.
-  asm volatile("" : "+v"(tid));
-  float mrun[E], num[E], den[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    mrun[e] = -INFINITY;
-    num[e] = 0.0f;
-    den[e] = 0.0f;
-  }
-  for (int j0 = first; j0 <= last; j0 += PB) {
-    float mj[E][PB], lj[E][PB], aj[E][PB];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int idx = min(tid + e * kThreads, G * D - 1);
-      const int h = idx / D, d = idx % D;
-#pragma unroll
-      for (int u = 0; u < PB; ++u) {  // `last` is uniform: no request past the last piece
-        const int64_t sl = (int64_t)item + j0 + u;
-        const bool have = j0 + u <= last;
-        mj[e][u] = have ? fetch(p.ws_m + sl * G + h) : -INFINITY;
-        lj[e][u] = have ? fetch(p.ws_l + sl * G + h) : 0.0f;
-        aj[e][u] = have ? fetch(p.ws_acc + (sl * G + h) * D + d) : 0.0f;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float mnew = mrun[e];
-#pragma unroll
-      for (int u = 0; u < PB; ++u)
-        if (j0 + u <= last) mnew = fmaxf(mnew, mj[e][u]);
-      const float sc = mrun[e] == -INFINITY ? 0.0f : fast_exp2(mrun[e] - mnew);
-      num[e] *= sc;
-      den[e] *= sc;
-#pragma unroll
-      for (int u = 0; u < PB; ++u) {
-        if (j0 + u > last) continue;
-        const float f = fast_exp2(mj[e][u] - mnew);
-        num[e] = fmaf(f, aj[e][u], num[e]);
-        den[e] = fmaf(f, lj[e][u], den[e]);
-      }
-      mrun[e] = mnew;
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int idx = tid + e * kThreads;
-    if (idx < G * D) {
-      const int h = idx / D, d = idx % D;
-      out[((int64_t)item * G + h) * D + d] = Store<DT>::cvt(num[e] / den[e]);
-    }
-  }
-}
-
 // MIN_WAVES: the minimum waves per SIMD the register allocation must allow
 // (1: no constraint).
 template <int DT, int D, int G, int NT, bool BS8, bool STEP, int MIN_WAVES>
@@ -872,6 +905,7 @@ void decode_flat_kernel(DecodeParams p) {
   __shared__ MergeLds<G, D> lds;
   __shared__ int s_wsum[kWaves];
   __shared__ int s_last;
+  __shared__ int s_pend_last;
   __shared__ int s_found;
 
   const int S = p.num_seqs;
@@ -949,6 +983,7 @@ void decode_flat_kernel(DecodeParams p) {
   __syncthreads();
   int seq = uniform_i32(s_found);
 
+  PendingPiece pend{-1, 0, 0};
   int pos = start;
   while (pos < end) {
     while (pos >= hkv * s_tc[seq + 1]) ++seq;  // skips empty sequences
@@ -961,7 +996,7 @@ void decode_flat_kernel(DecodeParams p) {
       int new_pos = -1;
       if (STEP && c.b == c.tiles && s_slot[seq] >= 0) new_pos = n - 1;
       run_segment<DT, D, G, NT, BS8>(p, seq, c.kh, 16 * c.a, min(16 * c.b, n), wave, lds,
-                                     new_pos, s_slot[seq]);
+                                     new_pos, s_slot[seq], pend, &s_pend_last);
     }
     __syncthreads();
     const SegCoords c = seg_coords(s_tc, seq, hkv, cost, pos, end);
@@ -987,26 +1022,31 @@ void decode_flat_kernel(DecodeParams p) {
       }
     }
     if (!whole) {
-      // Count this piece in; the item's last workgroup to arrive combines. The
-      // partials were written through to the device-coherent level (agent
-      // scope) and every thread waits for its writes to complete before the
-      // arrival is counted, so the last arriver, reading them back at agent
-      // scope, sees all of them. No L2 write-back or invalidate is needed.
-      const int last_w = (int)(((int64_t)(tile_base + tiles) * nwg - 1) / total);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (tid == 0)
-        s_last = __hip_atomic_fetch_add(p.ws_count + item, 1, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT) == last_w - first_w;
-      __syncthreads();
-      if (s_last) combine_pieces<DT, G, D>(p, out, item, first_w, last_w);
-      if (s_last) {
-        if (tid == 0)  // leave the counter zero for the next call
-          __hip_atomic_store(p.ws_count + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      // Counted in at the start of the range's next segment (see run_segment),
+      // or below when no segment follows. The item's last workgroup to arrive
+      // combines. The partials were written through to the device-coherent
+      // level (agent scope) and every thread waits for its writes to complete
+      // before the arrival is counted, so the last arriver, reading them back
+      // at agent scope, sees all of them. No L2 write-back or invalidate is
+      // needed.
+      pend = PendingPiece{item, first_w,
+                          (int)(((int64_t)(tile_base + tiles) * nwg - 1) / total)};
     }
     __syncthreads();  // lds and s_last are reused by the next segment
     pos = tile_base + b;
+  }
+  if (pend.item >= 0) {  // the range's last piece: no segment follows to overlap its count
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(p.ws_count + pend.item, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == pend.last - pend.first;
+    __syncthreads();
+    if (s_last) {
+      combine_pieces<DT, G, D>(p, out, pend.item, pend.first, pend.last);
+      if (tid == 0)  // leave the counter zero for the next call
+        __hip_atomic_store(p.ws_count + pend.item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   if (STEP) copy_new_rows<DT, D, G>(p, w + gridDim.x);
 }
