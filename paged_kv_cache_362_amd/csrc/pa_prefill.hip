@@ -11,12 +11,13 @@
 // Work: one workgroup (4 waves) per (sequence, KV head, tile of kPrefillRows
 // query rows); a query row is a (token, query head of the group) pair, so the
 // G heads that share a KV head share every K/V byte. Each wave owns 2 blocks
-// of 16 rows. The keys are walked in tiles of 32, assembled key by key
-// through the table (so block sizes 8-64 all work), double-buffered in LDS as
-// a K tile and a V tile, both [32 keys][D] row-major with rows padded by 16
-// bytes. The V operand of the second product (8 keys of one dim per lane, the
-// keys whose scores that lane holds) is read from the row-major V tile by
-// gfx950's transposing LDS read, so V is staged exactly as K is.
+// of 16 rows. The keys are walked in tiles of 32, assembled through the table
+// (so block sizes 8-64 all work) by gfx950's direct global -> LDS loads into
+// three LDS buffers (two tiles in flight while one is read), each a K tile
+// and a V tile, both [32 keys][D] row-major with the 16-byte chunks of each
+// row permuted (swz). The V operand of the second product (8 keys of one dim
+// per lane, the keys whose scores that lane holds) is read from the row-major
+// V tile by gfx950's transposing LDS read, so V is staged exactly as K is.
 //
 // Products, all on v_mfma_f32_16x16x32_{f16,bf16} with fp32 accumulation:
 //   S^T [16 keys x 16 rows] = K [keys x D] . Q^T [D x rows]     (2 key blocks)
@@ -48,14 +49,26 @@ template <int D, int QB> struct PfShape {
   static constexpr int KS = D / 32;                      // k-steps of the score product
   static constexpr int DB = D / 16;                      // 16-dim blocks of the output
   static constexpr int ROWS = kPfWaves * QB * 16;        // query rows per workgroup
-  static constexpr int KPITCH = D * 2 + 16;              // bytes per K or V row in LDS
+  static constexpr int KPITCH = D * 2;                   // bytes per K or V row in LDS
   static constexpr int KBYTES = kTileKeys * KPITCH;
   static constexpr int BUF = 2 * KBYTES;                 // one stage: K tile, V tile
   static constexpr int DCH = D / 8;                      // 16-byte chunks per row
   static constexpr int KCH_T = kTileKeys * DCH / kPfThreads;        // (key, column) items per thread
+  static constexpr int RPB = 256 / KPITCH;               // rows per 256 bytes (64 LDS banks)
   static_assert(kTileKeys * DCH % kPfThreads == 0, "K chunks must divide over the threads");
   static_assert(ROWS == kPrefillRows, "tile rows and host constant disagree");
 };
+
+// 16-byte chunk c of key k's row sits at chunk c ^ swz(k) of that row in
+// LDS. With m = (k / RPB) % DCH, swz moves m's low bits up by one and its top
+// bit down to bit 0, so that the 16 keys a K read takes at one column, and
+// the 8 consecutive keys of a transposing V read at one column pair, fall in
+// distinct 16-byte bank groups.
+template <int D> __device__ __forceinline__ uint32_t swz(uint32_t k) {
+  using S = PfShape<D, 2>;
+  const uint32_t m = (k / S::RPB) % S::DCH;
+  return ((m & (S::DCH / 2 - 1)) << 1) | (m / (S::DCH / 2));
+}
 
 template <int DT> __device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, f32x4 c);
 template <> __device__ __forceinline__ f32x4 mfma16<PA_F16>(const u32x4 &a, const u32x4 &b, f32x4 c) {
@@ -134,19 +147,24 @@ __device__ __forceinline__ uint2 lds_read_tr16(const char *p) {
   return __builtin_bit_cast(uint2, r);
 }
 
-// One stage of the global -> LDS pipeline: the table entries and the K/V
-// chunks of one key tile, held in registers by every thread.
+// Table entries of one key tile: a wave's 64 slots of one load are 64 / DCH
+// consecutive keys, aligned to that count, which divides every block size
+// (8 to 64), so they lie in one block and the entry is uniform across the
+// wave (scalar registers and a scalar load). Positions past the context are
+// clamped to its last one, which then lies in the wave's aligned group or
+// before it (all of the wave's keys clamped): the block is still the one the
+// wave's first key gives.
 template <int D> struct KVStage {
   using S = PfShape<D, 2>;
-  uint32_t phys[S::KCH_T];
-  u32x4 k[S::KCH_T], v[S::KCH_T];
+  int32_t phys[S::KCH_T];
 };
 
-// What each thread stages of a key tile, and how. Thread item p (p = tid +
-// 256 u) is key p % 32, 16-byte column p / 32, of both K and V: one table
-// entry and one address per item, and one 16-byte LDS store per tile. Keys
-// vary fastest across lanes, so with the padded rows a wave's stores spread
-// over the LDS banks.
+// What each thread stages of a key tile, and how. The tile's K (and V) rows
+// are staged by direct global -> LDS loads of 16 bytes per lane (lane i's
+// bytes land at the wave's LDS address plus 16 i), so a wave's load fills 64
+// consecutive 16-byte LDS slots, slot 64 (wave + 4 u) + lane.
+// Slot q holds key q / DCH, column chunk (q % DCH) ^ swz(key): so the 8 (or
+// 16) lanes of one key read its row's 128 (or 256) bytes from global memory.
 template <int D> struct Stager {
   using S = PfShape<D, 2>;
   const char *kbase;     // k_cache + kh * B * D elements, in bytes
@@ -157,16 +175,18 @@ template <int D> struct Stager {
   uint32_t bshift, bmask;
   uint32_t last_pos;     // context length - 1
   uint32_t key[S::KCH_T], col[S::KCH_T];  // item's key in the tile and byte column
-  uint32_t klds[S::KCH_T];
+  uint32_t slot0[S::KCH_T];               // LDS byte offset of the wave's 64 slots
+  uint32_t key0[S::KCH_T];                // the wave's first key of each load (uniform)
 
   __device__ void init(int tid) {
+    const int wave = tid / kWave, lane = tid % kWave;
 #pragma unroll
     for (int u = 0; u < S::KCH_T; ++u) {
-      const int p = tid + u * kPfThreads;
-      key[u] = p % kTileKeys;
-      const int c = p / kTileKeys;
-      col[u] = c * 16;
-      klds[u] = key[u] * S::KPITCH + col[u];
+      const int q = (wave + kPfWaves * u) * kWave + lane;
+      key[u] = q / S::DCH;
+      col[u] = ((q % S::DCH) ^ swz<D>(key[u])) * 16;
+      slot0[u] = (wave + kPfWaves * u) * kWave * 16;
+      key0[u] = __builtin_amdgcn_readfirstlane((wave + kPfWaves * u) * kWave / S::DCH);
     }
   }
   // Position of key `k` of tile j, clamped to the last cached position: keys
@@ -177,39 +197,62 @@ template <int D> struct Stager {
 
   __device__ void load_table(KVStage<D> &r, int j) const {
 #pragma unroll
-    for (int u = 0; u < S::KCH_T; ++u) r.phys[u] = uint32_t(table[pos_of(j, key[u]) >> bshift]);
+    for (int u = 0; u < S::KCH_T; ++u) {
+      // Read through the constant address space: the table is not written
+      // during the call, and the uniform load then goes through the scalar
+      // cache, apart from the vector-memory count the K/V loads are waited on.
+      typedef const __attribute__((address_space(4))) int32_t const_i32;
+      r.phys[u] = ((const_i32 *)table)[pos_of(j, key0[u]) >> bshift];
+    }
   }
-  __device__ void load_kv(KVStage<D> &r, int j) const {
+  // 2 * KCH_T loads (K, V per item), in that order.
+  __device__ void load_kv(const KVStage<D> &r, int j, char *buf) const {
+    typedef __attribute__((address_space(3))) void lds_void;
+    typedef __attribute__((address_space(1))) void glb_void;
 #pragma unroll
     for (int u = 0; u < S::KCH_T; ++u) {
       // Never address outside the pool, whatever the table holds. The entry
-      // is clamped here, at its use one tile after its load, not in
-      // load_table: there the clamp would make the wave wait for the table
-      // load (and every K/V load issued before it) within the same tile.
+      // is clamped here, at its use one tile after its load.
       const uint32_t phys = min(uint32_t(max(int(r.phys[u]), 0)), max_block);
       const uint64_t off = uint64_t(phys) * blk_bytes + ((pos_of(j, key[u]) & bmask) * (D * 2) + col[u]);
-      r.k[u] = *reinterpret_cast<const u32x4 *>(kbase + off);
-      r.v[u] = *reinterpret_cast<const u32x4 *>(vbase + off);
-    }
-  }
-  __device__ void store_lds(const KVStage<D> &r, char *buf) const {
-#pragma unroll
-    for (int u = 0; u < S::KCH_T; ++u) {
-      *reinterpret_cast<u32x4 *>(buf + klds[u]) = r.k[u];
-      *reinterpret_cast<u32x4 *>(buf + S::KBYTES + klds[u]) = r.v[u];
+      __builtin_amdgcn_global_load_lds((glb_void *)(kbase + off), (lds_void *)(buf + slot0[u]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void *)(vbase + off),
+                                       (lds_void *)(buf + S::KBYTES + slot0[u]), 16, 0, 0);
     }
   }
 };
 
-// head_dim 64 fits 128 VGPRs with no scratch when bounded: 4 waves per SIMD
-// instead of 3, which lets the softmax of one wave overlap the products of
-// more others (3% on the [1, 32, 8192, 64] call). head_dim 128 would spill
-// below ~204 VGPRs and stays unbounded (2 waves).
+// Workgroup barrier that waits for nothing: the LDS loads' completion is
+// waited for explicitly (wait_vm), and the compiler fences keep memory
+// accesses on their side of it.
+__device__ __forceinline__ void wg_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// s_waitcnt for at most N vector-memory operations and no LDS operation
+// outstanding (gfx9 encoding): before a barrier, this wave's reads of the
+// buffer that the next loads overwrite have completed.
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// head_dim 64 fits 128 VGPRs with no scratch when bounded: 4 waves per SIMD,
+// which lets the softmax of one wave overlap the products of more others.
+// head_dim 128 needs ~200 VGPRs and stays unbounded (2 waves).
 template <int DT, int D, int G, int QB, int NSET>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1)))
 void prefill_kernel(PrefillParams p) {
   using S = PfShape<D, QB>;
-  extern __shared__ __align__(16) char lds[];
+  static_assert(NSET == 3, "three LDS buffers");
+  // NSET = 3 K/V tile buffers: tile j is read from buffer j % 3 while the
+  // loads of tiles j + 1 and j + 2 land in the other two. Separate arrays, so
+  // the compiler sees that reading one does not wait for loads into another.
+  __shared__ __align__(16) char lds0[S::BUF];
+  __shared__ __align__(16) char lds1[S::BUF];
+  __shared__ __align__(16) char lds2[S::BUF];
 
   // Item of this workgroup. Workgroups are dispatched round-robin over the 8
   // XCDs; consecutive items (the query tiles of one (sequence, KV head), which
@@ -288,35 +331,50 @@ void prefill_kernel(PrefillParams p) {
   const uint32_t one2 = DT == PA_F16 ? 0x3C003C00u : 0x3F803F80u;  // two 1.0 elements
   const u32x4 ones = {one2, one2, one2, one2};
 
-  // Pipeline of NSET register stages and NSET LDS buffers: at the top of
-  // iteration j, stage (j + i) % NSET holds the loads in flight for tile j + i
-  // (0 < i < NSET), stage j % NSET is free and holds the table entries of tile
-  // j + NSET, and LDS buffer j % NSET holds tile j. Tiles past the last are clamped to it, and
-  // iterations past it compute with every key masked (no effect), so the loop
-  // runs a multiple of NSET iterations with compile-time stage indices.
+  // Per-lane LDS offsets of the operand reads (the chunk swizzle is a XOR
+  // with a per-lane value, so the per-step offsets are formed once here).
+  uint32_t koff[S::KS];
+  {
+    const uint32_t x = uint32_t(lg) ^ swz<D>(uint32_t(lr));
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) koff[ks] = lr * S::KPITCH + ((x ^ (4 * ks)) * 16);
+  }
+  const uint32_t vkey = 4 * lg + (lr >> 2);
+  const uint32_t vx = uint32_t((lr & 3) >> 1) ^ swz<D>(vkey);
+  const uint32_t vrow = vkey * S::KPITCH + (lr & 1) * 8;
+
+  // Pipeline: at the top of iteration j, buffer j % 3 holds tile j (every
+  // wave's loads of it complete, then a barrier), the loads of tile j + 1 are
+  // in flight into buffer (j + 1) % 3, and T[j % 3] holds the table entries of
+  // tile j + 2. Iteration j requests the entries of tile j + 3, then loads
+  // tile j + 2 into buffer (j + 2) % 3, which every wave finished reading in
+  // iteration j - 1. Tiles past the last are clamped to it (the loads are
+  // redundant but keep the count of loads per iteration fixed, which the wait
+  // before the barrier relies on), and iterations past it compute with every
+  // key masked (no effect), so the loop runs a multiple of 3 iterations with
+  // compile-time buffer indices.
   const int last = ntiles - 1;
-  KVStage<D> R[NSET];
+  char *const bufs[NSET] = {lds0, lds1, lds2};
+  KVStage<D> T[NSET];  // T[(t + 1) % NSET] holds the entries of tile t
 #pragma unroll
-  for (int i = 0; i < NSET; ++i) st.load_table(R[i], min(i, last));
-#pragma unroll
-  for (int i = 0; i < NSET; ++i) st.load_kv(R[i], min(i, last));
-  st.store_lds(R[0], lds);
-  st.load_table(R[0], min(NSET, last));
-  __syncthreads();
+  for (int t = 0; t < NSET - 1; ++t) {
+    st.load_table(T[(t + 1) % NSET], min(t, last));
+    st.load_kv(T[(t + 1) % NSET], min(t, last), bufs[t]);
+  }
+  st.load_table(T[0], min(NSET - 1, last));
+  wait_vm<S::KCH_T * 2 * (NSET - 2)>();  // tile 0 complete
+  wg_barrier();
 
   for (int j0 = 0; j0 < ntiles; j0 += NSET) {
 #pragma unroll
     for (int u = 0; u < NSET; ++u) {
       const int j = j0 + u;
-      KVStage<D> &mine = R[u];                  // free: gets tile j + NSET
-      KVStage<D> &next = R[(u + 1) % NSET];     // tile j + 1, in flight
-      // The table entries of tile j + NSET + 1 are requested before the K/V
-      // of tile j + NSET, so that waiting for them (next iteration) does not
-      // wait for these K/V loads too: loads complete in order.
-      st.load_table(next, min(j + NSET + 1, last));
-      st.load_kv(mine, min(j + NSET, last));
+      KVStage<D> &cur = T[u];                  // entries of tile j + NSET - 1
+      KVStage<D> &nxt = T[(u + 1) % NSET];     // gets the entries of tile j + NSET
+      st.load_table(nxt, min(j + NSET, last));
+      st.load_kv(cur, min(j + NSET - 1, last), bufs[(u + NSET - 1) % NSET]);
       const bool live = j < ntiles;
-      const char *kb_lds = lds + u * S::BUF;
+      const char *kb_lds = bufs[u];
       const char *vt_lds = kb_lds + S::KBYTES;
 
       // S^T = K . Q^T for 2 blocks of 16 keys.
@@ -327,8 +385,8 @@ void prefill_kernel(PrefillParams p) {
       for (int ks = 0; ks < S::KS; ++ks) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 a = *reinterpret_cast<const u32x4 *>(kb_lds + (16 * kb + lr) * S::KPITCH +
-                                                             (32 * ks + 8 * lg) * 2);
+          const u32x4 a =
+              *reinterpret_cast<const u32x4 *>(kb_lds + 16 * kb * S::KPITCH + koff[ks]);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma16<DT>(a, qreg[qb][ks], s[qb][kb]);
         }
@@ -405,11 +463,12 @@ void prefill_kernel(PrefillParams p) {
         lsum[qb] = mfma16<DT>(ones, ph[qb], lsum[qb]);
         if (DT == PA_BF16) lsum[qb] = mfma16<DT>(ones, pl[qb], lsum[qb]);
       }
-      const char *vt_lane = vt_lds + (4 * lg + (lr >> 2)) * S::KPITCH + (lr & 3) * 8;
+      const char *vt_lane = vt_lds + vrow;
 #pragma unroll
       for (int db = 0; db < S::DB; ++db) {
-        const uint2 lo = lds_read_tr16(vt_lane + 32 * db);
-        const uint2 hi = lds_read_tr16(vt_lane + 32 * db + 16 * S::KPITCH);
+        const uint32_t c = (vx ^ (2 * db)) * 16;
+        const uint2 lo = lds_read_tr16(vt_lane + c);
+        const uint2 hi = lds_read_tr16(vt_lane + c + 16 * S::KPITCH);
         const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
@@ -418,10 +477,14 @@ void prefill_kernel(PrefillParams p) {
         }
       }
 
-      st.store_lds(next, lds + ((u + 1) % NSET) * S::BUF);
-      __syncthreads();
+      // Tile j + 1 complete for this wave: only tile j + 2's loads were
+      // issued after its loads (the table entries take the scalar path).
+      // Then for every wave.
+      wait_vm<S::KCH_T * 2 * (NSET - 2)>();
+      wg_barrier();
     }
   }
+  wait_vm<0>();  // no load into this workgroup's LDS outlives its waves
 
   // out = acc / l for the valid rows. The row index is rebuilt from an
   // opaque copy of the lane so that no address of this store is computed
@@ -450,13 +513,12 @@ void prefill_kernel(PrefillParams p) {
 template <int DT, int D, int G>
 hipError_t launch_g(const PrefillParams &p, hipStream_t stream) {
   constexpr int QB = 2;
-  constexpr int NSET = 2;
-  using S = PfShape<D, QB>;
+  constexpr int NSET = 3;
   const int64_t items = int64_t(p.num_seqs) * p.num_kv_heads * p.q_tiles;
   if (items == 0) return hipSuccess;
   const int64_t grid = (items + 7) / 8 * 8;
   hipLaunchKernelGGL((prefill_kernel<DT, D, G, QB, NSET>), dim3(unsigned(grid)), dim3(kPfThreads),
-                     NSET * S::BUF, stream, p);
+                     0, stream, p);
   return hipGetLastError();
 }
 
