@@ -185,7 +185,7 @@ template <int D> struct Stager {
       const int q = (wave + kPfWaves * u) * kWave + lane;
       key[u] = q / S::DCH;
       col[u] = ((q % S::DCH) ^ swz<D>(key[u])) * 16;
-      slot0[u] = (wave + kPfWaves * u) * kWave * 16;
+      slot0[u] = __builtin_amdgcn_readfirstlane((wave + kPfWaves * u) * kWave * 16);
       key0[u] = __builtin_amdgcn_readfirstlane((wave + kPfWaves * u) * kWave / S::DCH);
     }
   }
@@ -213,10 +213,14 @@ template <int D> struct Stager {
     for (int u = 0; u < S::KCH_T; ++u) {
       // Never address outside the pool, whatever the table holds. The entry
       // is clamped here, at its use one tile after its load.
+      // The block's address is uniform (scalar registers); each lane adds its
+      // row and column as a 32-bit offset.
       const uint32_t phys = min(uint32_t(max(int(r.phys[u]), 0)), max_block);
-      const uint64_t off = uint64_t(phys) * blk_bytes + ((pos_of(j, key[u]) & bmask) * (D * 2) + col[u]);
-      __builtin_amdgcn_global_load_lds((glb_void *)(kbase + off), (lds_void *)(buf + slot0[u]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((glb_void *)(vbase + off),
+      const uint64_t blk = uint64_t(phys) * blk_bytes;
+      const uint32_t off = ((pos_of(j, key[u]) & bmask) * (D * 2)) | col[u];
+      __builtin_amdgcn_global_load_lds((glb_void *)(kbase + blk + off), (lds_void *)(buf + slot0[u]),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((glb_void *)(vbase + blk + off),
                                        (lds_void *)(buf + S::KBYTES + slot0[u]), 16, 0, 0);
     }
   }
@@ -241,7 +245,7 @@ template <int N> __device__ __forceinline__ void wait_vm() {
 
 // head_dim 64 fits 128 VGPRs with no scratch when bounded: 4 waves per SIMD,
 // which lets the softmax of one wave overlap the products of more others.
-// head_dim 128 needs ~200 VGPRs and stays unbounded (2 waves).
+// head_dim 128 is left unbounded and fits 168 (3 waves).
 template <int DT, int D, int G, int QB, int NSET>
 __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1)))
 void prefill_kernel(PrefillParams p) {
@@ -342,6 +346,11 @@ void prefill_kernel(PrefillParams p) {
   const uint32_t vkey = 4 * lg + (lr >> 2);
   const uint32_t vx = uint32_t((lr & 3) >> 1) ^ swz<D>(vkey);
   const uint32_t vrow = vkey * S::KPITCH + (lr & 1) * 8;
+  // At head_dim 64 the per-block offsets are formed once (4 VGPRs); at 128
+  // they are formed per tile, where 8 more live VGPRs cost more than the adds.
+  uint32_t voff[D == 64 ? S::DB : 1];
+#pragma unroll
+  for (int db = 0; db < (D == 64 ? S::DB : 1); ++db) voff[db] = vrow + (vx ^ (2 * db)) * 16;
 
   // Pipeline: at the top of iteration j, buffer j % 3 holds tile j (every
   // wave's loads of it complete, then a barrier), the loads of tile j + 1 are
@@ -463,12 +472,11 @@ void prefill_kernel(PrefillParams p) {
         lsum[qb] = mfma16<DT>(ones, ph[qb], lsum[qb]);
         if (DT == PA_BF16) lsum[qb] = mfma16<DT>(ones, pl[qb], lsum[qb]);
       }
-      const char *vt_lane = vt_lds + vrow;
 #pragma unroll
       for (int db = 0; db < S::DB; ++db) {
-        const uint32_t c = (vx ^ (2 * db)) * 16;
-        const uint2 lo = lds_read_tr16(vt_lane + c);
-        const uint2 hi = lds_read_tr16(vt_lane + c + 16 * S::KPITCH);
+        const uint32_t vo = D == 64 ? voff[D == 64 ? db : 0] : vrow + (vx ^ (2 * db)) * 16;
+        const uint2 lo = lds_read_tr16(vt_lds + vo);
+        const uint2 hi = lds_read_tr16(vt_lds + vo + 16 * S::KPITCH);
         const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
