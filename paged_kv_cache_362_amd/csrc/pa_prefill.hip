@@ -346,8 +346,9 @@ void prefill_kernel(PrefillParams p) {
   const uint32_t vkey = 4 * lg + (lr >> 2);
   const uint32_t vx = uint32_t((lr & 3) >> 1) ^ swz<D>(vkey);
   const uint32_t vrow = vkey * S::KPITCH + (lr & 1) * 8;
-  // At head_dim 64 the per-block offsets are formed once (4 VGPRs); at 128
-  // they are formed per tile, where 8 more live VGPRs cost more than the adds.
+  // At head_dim 64 the per-block offsets are formed once (4 VGPRs). At 128
+  // they are formed per tile: written as 8 values formed once, the kernel
+  // took 186-198 VGPRs instead of 166 and lost its third wave per SIMD.
   uint32_t voff[D == 64 ? S::DB : 1];
 #pragma unroll
   for (int db = 0; db < (D == 64 ? S::DB : 1); ++db) voff[db] = vrow + (vx ^ (2 * db)) * 16;
