@@ -325,9 +325,17 @@ void prefill_kernel(PrefillParams p) {
   // denominator uses exactly the rounded weights the numerator does).
   f32x4 acc[QB][S::DB], lsum[QB];
   float nm[QB];  // minus the running maximum (log2 domain), as the exponent FMA takes it
+  // head_dim 64: raw score above which a row's weight would exceed
+  // 2^kRescaleSlack, (kRescaleSlack + m) / scale_log2 (the scale is
+  // positive), so the test below needs no FMA. At 128 the two extra live
+  // VGPRs would cost the kernel its third wave per SIMD, and the test takes
+  // the FMA instead.
+  float thr[QB];
+  const float inv_scale_log2 = 1.f / p.scale_log2;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     nm[qb] = INFINITY;
+    thr[qb] = -INFINITY;
     lsum[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < S::DB; ++db) acc[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -427,9 +435,17 @@ void prefill_kernel(PrefillParams p) {
       bool raise = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        float mx = fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), fmaxf(s[qb][0][2], s[qb][0][3]));
-        mx = fmaxf(mx, fmaxf(fmaxf(s[qb][1][0], s[qb][1][1]), fmaxf(s[qb][1][2], s[qb][1][3])));
-        raise |= fmaf(mx, p.scale_log2, nm[qb]) > kRescaleSlack;
+        if (D == 64) {
+          // a chain of three-input maxima, against the raw-score threshold
+          float mx = fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), s[qb][0][2]);
+          mx = fmaxf(fmaxf(mx, s[qb][0][3]), s[qb][1][0]);
+          mx = fmaxf(fmaxf(mx, s[qb][1][1]), s[qb][1][2]);
+          raise |= fmaxf(mx, s[qb][1][3]) > thr[qb];
+        } else {
+          float mx = fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), fmaxf(s[qb][0][2], s[qb][0][3]));
+          mx = fmaxf(mx, fmaxf(fmaxf(s[qb][1][0], s[qb][1][1]), fmaxf(s[qb][1][2], s[qb][1][3])));
+          raise |= fmaf(mx, p.scale_log2, nm[qb]) > kRescaleSlack;
+        }
       }
       if (__any(raise)) {
 #pragma unroll
@@ -440,6 +456,7 @@ void prefill_kernel(PrefillParams p) {
           const float m_new = fmaxf(-nm[qb], group_max(mx) * p.scale_log2);
           const float alpha = fast_exp2(-nm[qb] - m_new);
           nm[qb] = -m_new;
+          if (D == 64) thr[qb] = (kRescaleSlack + m_new) * inv_scale_log2;
           lsum[qb] *= alpha;
 #pragma unroll
           for (int db = 0; db < S::DB; ++db) acc[qb][db] *= alpha;
