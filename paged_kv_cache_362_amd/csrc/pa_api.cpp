@@ -198,9 +198,13 @@ int flat_grid_size(const void *kernel, int threads, size_t dynamic_lds, int64_t 
     }
   }
   // Small calls: fewer, longer ranges (each workgroup has a fixed start-up cost
-  // and a split (sequence, KV head) costs a combine).
+  // and a split (sequence, KV head) costs a combine), but every compute unit
+  // streams unless the call is tiny.
   int64_t want = (max_tiles + kMinFlatTiles - 1) / kMinFlatTiles;
-  if (want < cus) want = cus;
+  int64_t floor_wgs = (max_tiles + kMinFlatTilesFloor - 1) / kMinFlatTilesFloor;
+  if (floor_wgs > cus) floor_wgs = cus;
+  if (want < floor_wgs) want = floor_wgs;
+  if (want < 1) want = 1;
   return want < resident ? int(want) : resident;
 }
 

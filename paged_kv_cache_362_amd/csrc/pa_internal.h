@@ -92,9 +92,14 @@ inline size_t flat_plan_lds_bytes(int num_seqs) { return size_t(3 * num_seqs + 1
 // Workgroups of a balanced launch on the current device: as many as can be
 // resident at once (capped at kMaxFlatWorkgroups), but no more than give each
 // kMinFlatTiles of `max_tiles` (an upper bound of the call's 16-token tiles,
-// from max_context_len), and at least one per compute unit. Defined in
-// pa_api.cpp.
+// from max_context_len), and at least one per compute unit or one per
+// kMinFlatTilesFloor tiles, whichever is fewer. Defined in pa_api.cpp.
 constexpr int kMinFlatTiles = 64;
+// The "one per compute unit" floor above is itself capped at one workgroup per
+// kMinFlatTilesFloor tiles of `max_tiles`: a tiny call (the 50-token, 4-head
+// one: 16 tiles) then gets one workgroup per (sequence, KV head) instead of
+// every head cut into one-tile pieces that pay the split-head combine.
+constexpr int kMinFlatTilesFloor = 4;
 // Overhead units charged per (sequence, KV head) by the balanced plan. Swept on
 // MI355X over 0, 4, 8, 16, 32 tiles: 4 was best (GQA-4 bf16 decode 2% faster
 // than 0; 16 and more lengthen every workload).

@@ -415,12 +415,24 @@ def test_balanced_form_reuses_its_workspace():
 
 
 def test_balanced_form_tiny_work_split_across_many_workgroups():
-    """16 tiles in all: most workgroups get no tile, each head is split over
-    several workgroups and combined by the last one."""
-    b = layouts.make_config(1, poison=True)
+    """16 tiles of work under a max_context_len bound of 4096 (a table 256
+    blocks wide): the grid is sized from the bound, so most workgroups get no
+    tile and each head is split over several workgroups and combined by the
+    last one. With the true bound (50) each head gets one workgroup."""
+    b = layouts.make_paged_batch(num_q_heads=4, num_kv_heads=4, head_dim=64, dtype="f32",
+                                 block_size=16, context_lens=[50], seed=1, poison=True,
+                                 num_blocks=320, fresh_block_write=True, extra_table_cols=252)
+    assert b.block_tables.shape[1] * 16 >= 4096
     _, _, o64 = oracle_step(b)
-    _, out = gpu_step(b)
-    assert_decode_close(layouts.from_device(out, "f32"), o64, "f32", "tiny balanced")
+    for bound in (b.max_context_len, 4096):
+        t = layouts.to_device(b, "cuda")
+        ops.reshape_and_cache(t["new_key"], t["new_value"], t["k_cache"], t["v_cache"],
+                              t["slot_mapping"])
+        out = ops.decode(t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                         t["context_lens"], b.scale, bound)
+        torch.cuda.synchronize()
+        assert_decode_close(layouts.from_device(out, "f32"), o64, "f32",
+                            f"tiny balanced, bound {bound}")
 
 
 def test_balanced_form_many_sequences_and_empty_ones():
