@@ -26,9 +26,9 @@
 // the softmax weights P^T feed the second product from the registers they are
 // in. The online softmax runs in the log2 domain with a running maximum per
 // row that is raised lazily (see kRescaleSlack); the row sums come from one
-// more MFMA per row block against an all-ones V^T block. Scores are masked only in the tiles that cross
-// a row's position. The scale must be positive (the tile maximum is taken on
-// unscaled scores).
+// more MFMA per row block against an all-ones V^T block. Scores are masked
+// only in the tiles that cross a row's position. The scale must be positive
+// (the tile maximum is taken on unscaled scores).
 //
 // Precision of P: fp16 weights carry 2^-11 relative error (the largest weight
 // is exactly 1), bf16 weights 2^-8, too much for a 2e-3 output bound, so the
