@@ -43,6 +43,8 @@ CASES = [
     ("f16", 8, 4, 128, 16, [1, 2, 31, 32, 33], [1, 2, 31, 32, 33]),  # tile edges
     ("bf16", 16, 2, 128, 16, [140, 77], [139, 77]),      # GQA 8 at D 128
     ("f16", 2, 1, 64, 16, [1000], [260]),                # long prefix, 3 row tiles
+    ("f16", 8, 4, 128, 8, [203, 57], [120, 57]),         # D 128 with 8-token blocks
+    ("bf16", 4, 4, 128, 8, [77], [77]),                  # (a wave stages 4 keys per load)
 ]
 
 
