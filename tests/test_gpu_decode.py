@@ -161,7 +161,7 @@ SHAPES = [
     ("f16", 8, 8, 128, 16), ("bf16", 8, 2, 128, 16), ("f32", 4, 4, 64, 16),
     ("f16", 8, 1, 64, 8), ("bf16", 16, 2, 64, 32), ("f16", 4, 2, 256, 64),
     ("f32", 8, 4, 128, 32), ("bf16", 2, 2, 256, 8), ("f32", 8, 1, 128, 16),
-    ("f16", 32, 4, 128, 32),
+    ("f16", 32, 4, 128, 32), ("bf16", 8, 2, 128, 8), ("f16", 4, 2, 128, 8),
 ]
 EDGE_LENS = [1, 2, 15, 16, 17, 31, 33, 63, 64, 65, 255, 256, 257, 511, 513, 1000]
 
